@@ -1,0 +1,345 @@
+"""Pins for the float64 oracle: each check ties it to something other than itself.
+
+Sources of truth: mpmath brute force at 50 digits, central finite differences, closed forms
+(all-zero E, V = 1, V = 2 logistic, equal classifier rows), torch's CPU cross-entropy and
+autograd in float64 (a library routine), algebraic invariants, and a pure-Python loop for the
+block filter.  tests/test_oracle_mutants.py plants mistakes in the oracle and checks that these
+pins catch them."""
+import math
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import cce_oracle as co
+
+II = -100
+
+
+def rand_case(seed, N, V, D, scale=1.0, ignore=()):
+    g = np.random.default_rng(seed)
+    E = g.standard_normal((N, D))
+    C = g.standard_normal((V, D)) * scale
+    t = g.integers(0, V, size=N)
+    for i in ignore:
+        t[i] = II
+    return E, C, t
+
+
+# ---------------------------------------------------------------- brute force (mpmath)
+def mp_loss_lse(E, C, t):
+    mpmath.mp.dps = 50
+    out = []
+    for n in range(E.shape[0]):
+        z = [mpmath.fsum(mpmath.mpf(float(E[n, d])) * mpmath.mpf(float(C[v, d]))
+                         for d in range(E.shape[1])) for v in range(C.shape[0])]
+        lse = mpmath.log(mpmath.fsum(mpmath.exp(x) for x in z))
+        loss = lse - z[t[n]] if t[n] != II else mpmath.mpf(0)
+        out.append((float(loss), float(lse)))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("seed,N,V,D", [(0, 6, 11, 5), (1, 8, 7, 3), (2, 3, 2, 4), (3, 5, 1, 2)])
+def test_forward_matches_mpmath(seed, N, V, D):
+    E, C, t = rand_case(seed, N, V, D, scale=2.0, ignore=(1,))
+    loss, lse = oracle.forward(E, C, t, II)
+    ref = mp_loss_lse(E, C, t)
+    np.testing.assert_allclose(loss, ref[:, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref[:, 1], rtol=0, atol=1e-12)
+    assert loss[1] == 0.0
+
+
+# ---------------------------------------------------------------- finite differences
+def weighted_loss(E, C, t, w):
+    loss, _ = oracle.forward(E, C, t, II)
+    return float((w * loss).sum())
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_gradients_match_central_differences(seed):
+    N, V, D = 5, 9, 4
+    E, C, t = rand_case(seed, N, V, D, ignore=(3,))
+    w = np.random.default_rng(seed + 10).uniform(0.5, 1.5, N)
+    dE, dC, _ = oracle.backward(E, C, t, w, II)
+    h = 1e-6
+    for X, dX in ((E, dE), (C, dC)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            old = X[idx]
+            X[idx] = old + h
+            fp = weighted_loss(E, C, t, w)
+            X[idx] = old - h
+            fm = weighted_loss(E, C, t, w)
+            X[idx] = old
+            num[idx] = (fp - fm) / (2 * h)
+        np.testing.assert_allclose(dX, num, rtol=1e-6, atol=1e-8)
+    assert np.all(dE[3] == 0.0)  # ignored row
+
+
+# ---------------------------------------------------------------- library cross-check
+def test_matches_torch_cross_entropy_and_autograd():
+    E, C, t = rand_case(5, 40, 70, 12, scale=1.5, ignore=(0, 7, 8))
+    w = np.random.default_rng(6).uniform(0.5, 1.5, 40)
+    Et = torch.tensor(E, requires_grad=True)
+    Ct = torch.tensor(C, requires_grad=True)
+    z = Et @ Ct.T
+    lt = torch.nn.functional.cross_entropy(z, torch.tensor(t), ignore_index=II, reduction="none")
+    (lt * torch.tensor(w)).sum().backward()
+    loss, lse = oracle.forward(E, C, t, II)
+    dE, dC, _ = oracle.backward(E, C, t, w, II)
+    np.testing.assert_allclose(loss, lt.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, torch.logsumexp(z, 1).detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dE, Et.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dC, Ct.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- closed forms
+def test_zero_embeddings_closed_form():
+    N, V, D = 17, 1000, 8
+    g = np.random.default_rng(3)
+    E = np.zeros((N, D))
+    C = g.standard_normal((V, D))
+    t = g.integers(0, V, N)
+    w = g.uniform(0.5, 1.5, N)
+    loss, lse = oracle.forward(E, C, t, II)
+    np.testing.assert_allclose(loss, math.log(V), rtol=0, atol=1e-12)   # 6.907755...
+    np.testing.assert_allclose(lse, math.log(V), rtol=0, atol=1e-12)
+    dE, dC, _ = oracle.backward(E, C, t, w, II)
+    assert np.all(dC == 0.0)
+    expect = w[:, None] * (C.mean(axis=0)[None, :] - C[t])
+    np.testing.assert_allclose(dE, expect, rtol=1e-10, atol=1e-12)
+
+
+def test_single_class_has_zero_loss_and_gradient():
+    E, C, t = rand_case(4, 6, 1, 3)
+    loss, lse = oracle.forward(E, C, t, II)
+    np.testing.assert_allclose(loss, 0.0, atol=1e-12)
+    np.testing.assert_allclose(lse, E @ C[0], atol=1e-12)
+    dE, dC, _ = oracle.backward(E, C, t, np.ones(6), II)
+    np.testing.assert_allclose(dE, 0.0, atol=1e-12)
+    np.testing.assert_allclose(dC, 0.0, atol=1e-12)
+
+
+def test_two_classes_is_logistic_loss():
+    E, C, t = rand_case(8, 30, 2, 6, scale=3.0)
+    loss, _ = oracle.forward(E, C, t, II)
+    z = E @ C.T
+    other = z[np.arange(30), 1 - t]
+    mine = z[np.arange(30), t]
+    softplus = np.logaddexp(0.0, other - mine)
+    np.testing.assert_allclose(loss, softplus, rtol=1e-13, atol=1e-14)
+
+
+def test_equal_classifier_rows_closed_form():
+    N, V, D = 12, 37, 5
+    g = np.random.default_rng(9)
+    E = g.standard_normal((N, D))
+    C = np.tile(g.standard_normal(D), (V, 1))
+    t = g.integers(0, V, N)
+    w = g.uniform(0.5, 1.5, N)
+    loss, _ = oracle.forward(E, C, t, II)
+    np.testing.assert_allclose(loss, math.log(V), atol=1e-12)
+    dE, dC, _ = oracle.backward(E, C, t, w, II)
+    np.testing.assert_allclose(dE, 0.0, atol=1e-12)
+    onehot = np.zeros((N, V))
+    onehot[np.arange(N), t] = 1.0
+    expect = (w[:, None] * (1.0 / V - onehot)).T @ E
+    np.testing.assert_allclose(dC, expect, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- invariants
+def test_forward_invariants():
+    E, C, t = rand_case(11, 50, 300, 16, scale=2.0, ignore=(4,))
+    loss, lse = oracle.forward(E, C, t, II, chunk=16, vchunk=64)
+    z = E @ C.T
+    zmax = z.max(axis=1)
+    assert np.all(lse >= zmax - 1e-12) and np.all(lse <= zmax + math.log(300) + 1e-12)
+    assert np.all(loss >= 0)
+    np.testing.assert_allclose(np.exp(z - lse[:, None]).sum(axis=1), 1.0, atol=1e-12)
+    # shift invariance: adding the same vector b to every classifier row shifts each token's
+    # logits by a constant, which cancels in the loss
+    b = np.random.default_rng(12).standard_normal(16)
+    loss2, lse2 = oracle.forward(E, C + b, t, II)
+    np.testing.assert_allclose(loss2, loss, atol=1e-10)
+    np.testing.assert_allclose(lse2 - lse, E @ b, atol=1e-10)
+
+
+def test_dominant_logit_no_overflow():
+    N, V, D = 4, 50, 4
+    E = 100.0 * np.eye(N, D)
+    C = np.zeros((V, D))
+    t = np.array([3, 5, 7, 9])
+    C[t, np.arange(N)] = 10.0   # each token's target logit is 1000, all its other logits 0
+    loss, lse = oracle.forward(E, C, t, II)
+    assert np.all(np.isfinite(loss)) and np.all(np.isfinite(lse))
+    np.testing.assert_allclose(lse, 1000.0, atol=1e-12)
+    np.testing.assert_allclose(loss, 0.0, atol=1e-12)
+
+
+def test_gradient_invariants():
+    E, C, t = rand_case(13, 64, 200, 10, scale=2.0, ignore=(5, 6))
+    w = np.random.default_rng(14).uniform(0.5, 1.5, 64)
+    dE, dC, _ = oracle.backward(E, C, t, w, II, chunk=64, vchunk=64)
+    np.testing.assert_allclose(dC.sum(axis=0), 0.0, atol=1e-11)          # sum_v p = 1
+    np.testing.assert_allclose(E.T @ dE, dC.T @ C, rtol=1e-10, atol=1e-10)  # both from one G
+    dE2, dC2, _ = oracle.backward(E, C, t, 2.5 * w, II)
+    np.testing.assert_allclose(dE2, 2.5 * dE, rtol=1e-12, atol=1e-13)       # linear in dloss
+    np.testing.assert_allclose(dC2, 2.5 * dC, rtol=1e-12, atol=1e-13)
+    dEs, dCs, _ = oracle.backward(E, C, t, 0.75, II)                        # scalar dloss
+    dEv, dCv, _ = oracle.backward(E, C, t, np.full(64, 0.75), II)
+    np.testing.assert_array_equal(dEs, dEv)
+    np.testing.assert_array_equal(dCs, dCv)
+
+
+def test_chunking_does_not_change_results():
+    E, C, t = rand_case(15, 70, 130, 8, ignore=(2,))
+    a = oracle.forward(E, C, t, II, chunk=256, vchunk=65536)
+    b = oracle.forward(E, C, t, II, chunk=64, vchunk=64)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-12)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-12)
+
+
+def test_out_of_range_target_is_an_error():
+    E, C, t = rand_case(16, 4, 10, 3)
+    t[2] = 10
+    with pytest.raises(ValueError):
+        oracle.forward(E, C, t, II)
+    t[2] = -1
+    with pytest.raises(ValueError):
+        oracle.forward(E, C, t, II)
+
+
+# ---------------------------------------------------------------- gradient filtering
+def brute_filtered_grads(E, C, t, w, eps, bn, bv):
+    """Plain loops: per-element p, per-block decision, then the filtered G products."""
+    N, V = E.shape[0], C.shape[0]
+    z = [[float(np.dot(E[n], C[v])) for v in range(V)] for n in range(N)]
+    G = np.zeros((N, V))
+    P = np.zeros((N, V))
+    for n in range(N):
+        m = max(z[n])
+        s = sum(math.exp(x - m) for x in z[n])
+        for v in range(V):
+            P[n, v] = math.exp(z[n][v] - m) / s
+            if t[n] != II:
+                G[n, v] = w[n] * (P[n, v] - (1.0 if v == t[n] else 0.0))
+    skipped = 0
+    for i in range(0, N, bn):
+        for j in range(0, V, bv):
+            significant = False
+            for n in range(i, min(N, i + bn)):
+                if t[n] == II:
+                    continue
+                for v in range(j, min(V, j + bv)):
+                    if P[n, v] >= eps or v == t[n]:
+                        significant = True
+            if not significant and eps > 0:
+                skipped += 1
+                G[i:i + bn, j:j + bv] = 0.0
+    return G @ C, G.T @ E, skipped
+
+
+@pytest.mark.parametrize("eps", [0.0, 2.0 ** -12, 0.02])
+def test_block_filter_matches_brute_force(eps):
+    E, C, t = rand_case(21, 20, 45, 6, scale=2.5, ignore=(3, 17))
+    w = np.random.default_rng(22).uniform(0.5, 1.5, 20)
+    dE, dC, (sk, tot) = oracle.backward(E, C, t, w, II, filter_eps=eps, block_n=4, block_v=8,
+                                        chunk=8, vchunk=16)
+    bE, bC, bsk = brute_filtered_grads(E, C, t, w, eps, 4, 8)
+    assert sk == bsk and tot == 5 * 6
+    np.testing.assert_allclose(dE, bE, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dC, bC, rtol=1e-10, atol=1e-12)
+    if eps == 0.02:
+        assert 0 < sk < tot  # the case exercises both outcomes
+
+
+def test_filter_eps_zero_is_bitwise_unfiltered():
+    E, C, t = rand_case(23, 30, 90, 7, scale=3.0)
+    w = np.ones(30)
+    a = oracle.backward(E, C, t, w, II)
+    b = oracle.backward(E, C, t, w, II, filter_eps=0.0, block_n=64, block_v=64)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    assert a[2][0] == 0
+
+
+def test_far_vocabulary_blocks_are_skipped_exactly():
+    """Vocab blocks 1 and 3 (of 5, 64 wide) get logits near -200 for every token, so every
+    (token block, far vocab block) pair is negligible; targets avoid them."""
+    N, V, D, bn, bv = 150, 320, 4, 64, 64
+    g = np.random.default_rng(31)
+    E = np.zeros((N, D))
+    E[:, 0] = 10.0
+    E[:, 1:] = g.standard_normal((N, D - 1)) * 0.1
+    C = g.standard_normal((V, D)) * 0.05
+    far = np.r_[64:128, 192:256]
+    C[far, 0] = -20.0
+    near = np.setdiff1d(np.arange(V), far)
+    t = g.choice(near, size=N)
+    dE, dC, (sk, tot) = oracle.backward(E, C, t, np.ones(N), II, filter_eps=2.0 ** -12)
+    assert tot == 3 * 5
+    assert sk == 3 * 2
+    dE0, dC0, _ = oracle.backward(E, C, t, np.ones(N), II)
+    assert np.linalg.norm(dC - dC0) / np.linalg.norm(dC0) < 1e-12
+    # a target inside a far block keeps that one block (its G entry is about -1)
+    t[70] = 200
+    _, _, (sk2, _) = oracle.backward(E, C, t, np.ones(N), II, filter_eps=2.0 ** -12)
+    assert sk2 == 3 * 2 - 1
+    # the same target on an ignored row does not
+    t[70] = II
+    _, _, (sk3, _) = oracle.backward(E, C, t, np.ones(N), II, filter_eps=2.0 ** -12)
+    assert sk3 == 3 * 2
+
+
+def test_token_rows_equals_full_problem_restricted():
+    E, C, t = rand_case(41, 200, 300, 6, scale=3.0, ignore=(70, 130))
+    w = np.zeros(200)
+    rows = np.r_[64:128, 192:200]       # one whole block and the ragged last block
+    w[rows] = np.random.default_rng(42).uniform(0.5, 1.5, len(rows))
+    for eps in (0.0, 0.01):
+        dE, dC, (sk, _) = oracle.backward(E, C, t, w, II, filter_eps=eps)
+        loss, lse = oracle.forward(E, C, t, II)
+        r = oracle.token_rows(E, C, t, rows, w[rows], II, filter_eps=eps, vchunk=128)
+        np.testing.assert_allclose(r["loss"], loss[rows], atol=1e-12)
+        np.testing.assert_allclose(r["lse"], lse[rows], atol=1e-12)
+        np.testing.assert_allclose(r["dE"], dE[rows], rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(r["dC_part"], dC, rtol=1e-10, atol=1e-13)
+
+
+def test_loss_mean():
+    E, C, t = rand_case(51, 40, 60, 5, ignore=(1, 2, 3))
+    m, dE, dC, nv = oracle.loss_mean(E, C, t, II)
+    loss, _ = oracle.forward(E, C, t, II)
+    assert nv == 37
+    assert m == pytest.approx(loss.sum() / 37, rel=1e-14)
+    bE, bC, _ = oracle.backward(E, C, t, np.full(40, 1 / 37), II)
+    np.testing.assert_allclose(dE, bE, rtol=1e-14)
+    np.testing.assert_allclose(dC, bC, rtol=1e-14)
+    t[:] = II
+    m, dE, dC, nv = oracle.loss_mean(E, C, t, II)
+    assert (m, nv) == (0.0, 0) and not dE.any() and not dC.any()
+
+
+def test_oracle_reproduces_its_regression_fixture():
+    import json
+    import os
+    import cce_synth as S
+    with open(os.path.join(os.path.dirname(__file__), "golden", "oracle_small_case.json")) as f:
+        g = json.load(f)
+    c = g["case"]
+    d = S.small_case(N=c["N"], D=c["D"], V=c["V"], dtype=c["dtype"], seed=c["seed"],
+                     c_scale=c["c_scale"], zipf_s=c["zipf_s"], ignore_frac=c["ignore_frac"])
+    assert d["targets"].tolist() == g["targets"]
+    w = S.dloss_weights(c["dloss_seed"], c["N"])
+    loss, lse = oracle.forward(d["E"], d["C"], d["targets"], II)
+    dE, dC, (sk, tot) = oracle.backward(d["E"], d["C"], d["targets"], w, II,
+                                        filter_eps=c["filter_eps"], block_n=c["block_n"],
+                                        block_v=c["block_v"])
+    np.testing.assert_allclose(loss, g["loss"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, g["lse"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dE.sum(1), g["dE_rowsum"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dC.sum(1), g["dC_rowsum"], rtol=0, atol=1e-12)
+    assert (sk, tot) == (g["skipped"], g["total"])
+    assert 0 < sk < tot
