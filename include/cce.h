@@ -1,0 +1,120 @@
+/*
+ * libcce: Cut Cross-Entropy for AMD MI355X (gfx950), C ABI.
+ *
+ * The operation (the Cut Cross-Entropy abstract on taxoreview.com, page dblp:393/3562,
+ * sentences 3-6): for token embeddings E [N,D] and classifier rows C [V,D],
+ *
+ *     z[n,v]  = E[n,:] . C[v,:]                         (logits, never written to memory)
+ *     lse[n]  = log sum_v exp(z[n,v])                    (log-sum-exp over the vocabulary)
+ *     loss[n] = lse[n] - z[n, t[n]]     (0 when t[n] == ignore_index)
+ *
+ * and its gradients dE = G C, dC = G^T E with G[n,v] = dloss[n] (softmax[n,v] - [v == t[n]]),
+ * where the backward skips gradient blocks whose softmax entries are all below filter_eps
+ * (same abstract, sentence 9).  The N x V logit matrix is never materialised in device memory.
+ *
+ * Conventions shared by every call:
+ *   - E and C are row-major and contiguous, of the same dtype (cce_dtype); D is the row length.
+ *   - targets is int64 [N]; a row whose target equals ignore_index is "ignored": its loss is 0,
+ *     its gradient rows are 0, and it never makes a filter block significant.
+ *   - All array arguments are device pointers into memory the caller owns (hipMalloc or a
+ *     framework allocator).  The library never allocates or frees device memory and keeps no
+ *     per-call state; scratch memory is the caller's workspace (query its size first).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work on
+ *     that stream and returns; no host synchronisation happens inside.  Calls that share a
+ *     workspace must not run concurrently on different streams.
+ *   - Argument errors are detected on the host before anything is enqueued, and reported as
+ *     CCE_ERR_INVALID_ARGUMENT / CCE_ERR_UNSUPPORTED / CCE_ERR_WORKSPACE_TOO_SMALL; launch
+ *     failures as CCE_ERR_HIP.  N == 0 is a valid no-op.
+ *   - Validity: N >= 0, V >= 1, D >= 1, D % 8 == 0 for bf16 and D % 4 == 0 for fp32,
+ *     N, V, D < 2^31, non-null pointers when N > 0, filter_eps finite and >= 0.
+ *   - Limits of the gfx950 kernels (CCE_ERR_UNSUPPORTED beyond them): N <= 2^24, V <= 2^24,
+ *     D <= 65536.
+ */
+#ifndef LIBCCE_CCE_H
+#define LIBCCE_CCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CCE_OK = 0,
+  CCE_ERR_INVALID_ARGUMENT = 1,
+  CCE_ERR_UNSUPPORTED = 2,
+  CCE_ERR_WORKSPACE_TOO_SMALL = 3,
+  CCE_ERR_HIP = 4
+} cce_status;
+
+typedef enum { CCE_F32 = 0, CCE_BF16 = 1 } cce_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* cce_status_string(cce_status s);
+
+/* Device workspace bytes needed by cce_forward / cce_backward / cce_loss_mean for a problem.
+ * Pure host functions.  Each formula is linear in N for fixed V and D (no N*V term):
+ *   forward : splits * N * 8 bytes, splits <= 256 vocabulary ranges (an on-chip LSE partial
+ *             per token and range), rounded to 256 bytes;
+ *   backward: roundup(N,256) * Vc * sizeof(dtype) for one vocabulary chunk of the
+ *             softmax-gradient tile store (Vc <= 8192 columns), plus its 64x64 block flags;
+ *   mean    : forward + backward + 8 * roundup(N,64) + 256.
+ * Returns 0 for invalid sizes. */
+size_t cce_forward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dtype);
+size_t cce_backward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dtype);
+size_t cce_loss_mean_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dtype);
+
+/* Forward (abstract sentences 4-6): per-token loss and log-sum-exp.
+ *   E [N,D], C [V,D]     dtype `dtype`, device, read only.
+ *   targets [N]          int64, device.  Values outside [0,V) other than ignore_index are
+ *                        errors found on the device: that row's loss is NaN and *err_flag is
+ *                        set to 1 (if err_flag is non-NULL); read it after synchronising.
+ *   loss [N], lse [N]    fp32, device, written.  lse is the natural-log LSE; it is written
+ *                        for ignored rows too.
+ *   ws, ws_bytes         device workspace of at least cce_forward_workspace_bytes().
+ *   err_flag             device int32 or NULL; only ever set to 1, never cleared. */
+cce_status cce_forward(const void* E, const void* C, const int64_t* targets,
+                       int64_t N, int64_t V, int64_t D, cce_dtype dtype, int64_t ignore_index,
+                       float* loss, float* lse, void* ws, size_t ws_bytes, int32_t* err_flag,
+                       void* stream);
+
+/* Backward (abstract sentences 4 and 9): dE and dC of sum_n dloss[n] * loss[n].
+ *   dloss                fp32, device: [N] when dloss_stride == 1, one scalar when 0.
+ *   E, C, targets        as in cce_forward.  Invalid targets do not fault; their rows get no
+ *                        one-hot term (the forward reports them).
+ *   lse [N]              fp32, device: the lse written by cce_forward for the same E, C.
+ *   filter_eps           gradient filtering threshold on softmax values (not scaled by dloss);
+ *                        0 disables it.  A 64-token x 64-vocabulary block of G is skipped when
+ *                        all of its softmax entries are < filter_eps and it holds no target of
+ *                        a non-ignored row.  2^-12 is the threshold used by the benchmarks.
+ *   dE [N,D], dC [V,D]   fp32, device, overwritten (no need to clear them first).
+ *   ws, ws_bytes         device workspace of at least cce_backward_workspace_bytes().
+ *   skip_stats           device int64[2] or NULL: [0] = skipped 64x64 blocks,
+ *                        [1] = all blocks, ceil(N/64) * ceil(V/64). */
+cce_status cce_backward(const float* dloss, int64_t dloss_stride, const void* E, const void* C,
+                        const int64_t* targets, const float* lse, int64_t N, int64_t V,
+                        int64_t D, cce_dtype dtype, int64_t ignore_index, float filter_eps,
+                        float* dE, float* dC, void* ws, size_t ws_bytes, int64_t* skip_stats,
+                        void* stream);
+
+/* Mean-reduced convenience call: loss_mean = sum over non-ignored rows of loss / N_valid and
+ * the gradients of that mean (dloss = 1 / N_valid for every row).  With N_valid == 0 the mean
+ * and both gradients are 0.  loss_mean and n_valid (NULL allowed) are device scalars.
+ *   ws: at least cce_loss_mean_workspace_bytes(); err_flag, skip_stats as above. */
+cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, int64_t N,
+                         int64_t V, int64_t D, cce_dtype dtype, int64_t ignore_index,
+                         float filter_eps, float* loss_mean, int64_t* n_valid, float* dE,
+                         float* dC, void* ws, size_t ws_bytes, int32_t* err_flag,
+                         int64_t* skip_stats, void* stream);
+
+/* Launch-shape introspection for reports (pure host): the vocabulary split count of the
+ * forward and the vocabulary chunk width Vc of the backward for a problem. */
+int64_t cce_forward_splits(int64_t N, int64_t V, int64_t D, cce_dtype dtype);
+int64_t cce_backward_chunk(int64_t N, int64_t V, int64_t D, cce_dtype dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBCCE_CCE_H */

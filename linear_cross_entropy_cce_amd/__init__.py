@@ -1,0 +1,13 @@
+"""Cut Cross-Entropy for AMD MI355X (gfx950): Python binding of libcce.
+
+The classifier-head cross-entropy loss, lse_v(E C_v^T) - E C_target^T, and its gradients dE and
+dC, computed by hand-written HIP kernels without writing the N x V logits to device memory
+(the Cut Cross-Entropy abstract, taxoreview.com page dblp:393/3562, sentences 4-6 and 9).
+"""
+from ._lib import (CCEError, LIB_PATH, backward_chunk, backward_workspace_bytes, cce_backward,
+                   cce_forward, cce_loss_mean, forward_splits, forward_workspace_bytes, lib,
+                   loss_mean_workspace_bytes)
+
+__all__ = ["CCEError", "LIB_PATH", "backward_chunk", "backward_workspace_bytes", "cce_backward",
+           "cce_forward", "cce_loss_mean", "forward_splits", "forward_workspace_bytes", "lib",
+           "loss_mean_workspace_bytes"]

@@ -1,0 +1,178 @@
+"""ctypes binding of libcce (include/cce.h): argument marshalling only.
+
+Every step of the computation runs in the HIP kernels of libcce.so; this module only turns torch
+tensors into device pointers, sizes and the current HIP stream, allocates outputs and
+workspaces with torch (device memory plumbing) and maps status codes to exceptions.  There is
+no CPU fallback: if libcce.so is missing or no GPU is present, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcce.so")
+
+CCE_F32, CCE_BF16 = 0, 1
+_STATUS = {0: "CCE_OK", 1: "CCE_ERR_INVALID_ARGUMENT", 2: "CCE_ERR_UNSUPPORTED",
+           3: "CCE_ERR_WORKSPACE_TOO_SMALL", 4: "CCE_ERR_HIP"}
+
+_lib = None
+
+_c_ptr, _i64, _sz, _i32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+
+# name -> (restype, argtypes); the C ABI declared in include/cce.h
+SIGNATURES = {
+    "cce_status_string": (ctypes.c_char_p, [_i32]),
+    "cce_forward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "cce_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "cce_loss_mean_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "cce_forward_splits": (_i64, [_i64, _i64, _i64, _i32]),
+    "cce_backward_chunk": (_i64, [_i64, _i64, _i64, _i32]),
+    "cce_forward": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _c_ptr, _c_ptr,
+                           _c_ptr, _sz, _c_ptr, _c_ptr]),
+    "cce_backward": (_i32, [_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32,
+                            _i64, _f32, _c_ptr, _c_ptr, _c_ptr, _sz, _c_ptr, _c_ptr]),
+    "cce_loss_mean": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _f32, _c_ptr,
+                             _c_ptr, _c_ptr, _c_ptr, _c_ptr, _sz, _c_ptr, _c_ptr, _c_ptr]),
+}
+
+
+class CCEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libcce.so once.  torch is imported first so that the HIP runtime it carries (same
+    soname as the one libcce links) is the one both use."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m "
+                               "linear_cross_entropy_cce_amd.build` (hipcc, gfx950)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return CCE_BF16
+    if t == torch.float32:
+        return CCE_F32
+    raise TypeError(f"E and C must be bfloat16 or float32, not {t}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise CCEError(fn, status)
+
+
+def _check_inputs(E, C, targets):
+    for name, t in (("E", E), ("C", C), ("targets", targets)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if E.dim() != 2 or C.dim() != 2 or E.shape[1] != C.shape[1]:
+        raise ValueError(f"E [N,D] and C [V,D] expected, got {tuple(E.shape)}, {tuple(C.shape)}")
+    if E.dtype != C.dtype:
+        raise TypeError("E and C must have the same dtype")
+    if targets.dtype != torch.int64 or targets.shape != (E.shape[0],):
+        raise ValueError("targets must be int64 [N]")
+    return E.shape[0], C.shape[0], E.shape[1], dtype_code(E.dtype)
+
+
+def forward_workspace_bytes(N: int, V: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().cce_forward_workspace_bytes(N, V, D, dtype_code(dtype)))
+
+
+def backward_workspace_bytes(N: int, V: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().cce_backward_workspace_bytes(N, V, D, dtype_code(dtype)))
+
+
+def loss_mean_workspace_bytes(N: int, V: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().cce_loss_mean_workspace_bytes(N, V, D, dtype_code(dtype)))
+
+
+def forward_splits(N: int, V: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().cce_forward_splits(N, V, D, dtype_code(dtype)))
+
+
+def backward_chunk(N: int, V: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().cce_backward_chunk(N, V, D, dtype_code(dtype)))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def cce_forward(E, C, targets, ignore_index: int = -100, *, loss=None, lse=None, ws=None,
+                err_flag=None, stream=None):
+    """Per-token loss and LSE (fp32 [N]).  Returns (loss, lse)."""
+    N, V, D, dt = _check_inputs(E, C, targets)
+    dev = E.device
+    loss = torch.empty(N, dtype=torch.float32, device=dev) if loss is None else loss
+    lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else lse
+    need = lib().cce_forward_workspace_bytes(N, V, D, dt)
+    ws = workspace(need, dev) if ws is None else ws
+    _check("cce_forward", lib().cce_forward(
+        _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, _ptr(loss), _ptr(lse),
+        _ptr(ws), ws.numel() * ws.element_size(), _ptr(err_flag), _stream(stream)))
+    return loss, lse
+
+
+def cce_backward(dloss, E, C, targets, lse, ignore_index: int = -100, filter_eps: float = 0.0,
+                 *, dE=None, dC=None, ws=None, skip_stats=None, stream=None):
+    """dE [N,D] and dC [V,D] (fp32).  dloss: fp32 [N], or a 1-element tensor (scalar)."""
+    N, V, D, dt = _check_inputs(E, C, targets)
+    dev = E.device
+    if dloss.dtype != torch.float32 or not dloss.is_cuda:
+        raise ValueError("dloss must be a float32 GPU tensor")
+    stride = 0 if dloss.numel() == 1 and N != 1 else 1
+    if stride == 1 and dloss.shape != (N,):
+        raise ValueError("dloss must have N elements or one")
+    dE = torch.empty((N, D), dtype=torch.float32, device=dev) if dE is None else dE
+    dC = torch.empty((V, D), dtype=torch.float32, device=dev) if dC is None else dC
+    need = lib().cce_backward_workspace_bytes(N, V, D, dt)
+    ws = workspace(need, dev) if ws is None else ws
+    _check("cce_backward", lib().cce_backward(
+        _ptr(dloss), stride, _ptr(E), _ptr(C), _ptr(targets), _ptr(lse), N, V, D, dt,
+        ignore_index, float(filter_eps), _ptr(dE), _ptr(dC), _ptr(ws),
+        ws.numel() * ws.element_size(), _ptr(skip_stats), _stream(stream)))
+    return dE, dC
+
+
+def cce_loss_mean(E, C, targets, ignore_index: int = -100, filter_eps: float = 0.0, *,
+                  dE=None, dC=None, ws=None, err_flag=None, skip_stats=None, stream=None):
+    """Mean loss over non-ignored tokens and its gradients.  Returns (mean[1], n_valid[1],
+    dE, dC) as device tensors."""
+    N, V, D, dt = _check_inputs(E, C, targets)
+    dev = E.device
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+    n_valid = torch.empty(1, dtype=torch.int64, device=dev)
+    dE = torch.empty((N, D), dtype=torch.float32, device=dev) if dE is None else dE
+    dC = torch.empty((V, D), dtype=torch.float32, device=dev) if dC is None else dC
+    need = lib().cce_loss_mean_workspace_bytes(N, V, D, dt)
+    ws = workspace(need, dev) if ws is None else ws
+    _check("cce_loss_mean", lib().cce_loss_mean(
+        _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, float(filter_eps),
+        _ptr(mean), _ptr(n_valid), _ptr(dE), _ptr(dC), _ptr(ws), ws.numel() * ws.element_size(),
+        _ptr(err_flag), _ptr(skip_stats), _stream(stream)))
+    return mean, n_valid, dE, dC

@@ -1,0 +1,295 @@
+// libcce C ABI: argument validation, launch planning and kernel launches (include/cce.h).
+//
+// Host-side plan for the Cut Cross-Entropy abstract's method (taxoreview.com page
+// dblp:393/3562, sentences 4-6 and 9):
+//   forward : k_fwd_lse over (token tile x vocabulary range), then k_fwd_finish;
+//   backward: for each vocabulary chunk of Vc rows, k_bwd_g -> k_bwd_dc -> k_bwd_de on the
+//             caller's stream; only the chunk's G tiles (N x Vc) ever live in the workspace.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "cce.h"
+#include "cce_kernels.hpp"
+
+namespace {
+
+using namespace cce;
+
+constexpr int64_t kMaxRows = int64_t(1) << 24;
+constexpr int64_t kMaxD = 65536;
+constexpr int kAssumedCUs = 256;  // MI355X; only shapes the launch plan, never correctness
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t dtype_size(cce_dtype dt) { return dt == CCE_BF16 ? 2 : 4; }
+
+bool sizes_ok(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
+  if (dt != CCE_F32 && dt != CCE_BF16) return false;
+  if (N < 0 || V < 1 || D < 1) return false;
+  if (D % (dt == CCE_BF16 ? 8 : 4) != 0) return false;
+  return true;
+}
+bool sizes_supported(int64_t N, int64_t V, int64_t D) {
+  return N <= kMaxRows && V <= kMaxRows && D <= kMaxD;
+}
+
+// Number of vocabulary ranges of the forward.  Cost model: waves of workgroups times tiles per
+// workgroup; among plans within 3% of the best, prefer 8 ranges, which with 4 token tiles
+// fills one XCD's 32 CUs with 4 + 8 distinct operand tiles.
+int64_t plan_splits(int64_t N, int64_t V) {
+  const int64_t n_tb = ceil_div(std::max<int64_t>(N, 1), kTile), n_vt = ceil_div(V, kTile);
+  const int64_t smax = std::min<int64_t>(n_vt, 256);
+  double best = 1e300;
+  std::vector<double> cost(smax + 1, 0.0);
+  for (int64_t s = 1; s <= smax; ++s) {
+    cost[s] = (double)ceil_div(n_tb * s, kAssumedCUs) * (double)ceil_div(n_vt, s);
+    best = std::min(best, cost[s]);
+  }
+  int64_t pick = 1;
+  double pick_dist = 1e300;
+  for (int64_t s = 1; s <= smax; ++s) {
+    if (cost[s] > best * 1.03) continue;
+    const double dist = std::fabs(std::log2((double)s) - 3.0);
+    if (dist < pick_dist) { pick_dist = dist; pick = s; }
+  }
+  return pick;
+}
+
+int64_t env_int(const char* name, int64_t dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  char* end = nullptr;
+  const long long x = std::strtoll(v, &end, 10);
+  return (end && *end == 0 && x > 0) ? (int64_t)x : dflt;
+}
+
+// Vocabulary chunk width of the backward (multiple of 256).  CCE_VC overrides the default.
+int64_t plan_chunk(int64_t V) {
+  static const int64_t vc_env = env_int("CCE_VC", 8192);
+  int64_t vc = std::max<int64_t>(256, std::min<int64_t>(vc_env, 8192) / 256 * 256);
+  return std::min<int64_t>(vc, ceil_div(V, kTile) * kTile);
+}
+
+struct BwdLayout {
+  int64_t n_pad, vc, fstride;
+  size_t g_bytes, flag_bytes, total;
+};
+BwdLayout bwd_layout(int64_t N, int64_t V, cce_dtype dt) {
+  BwdLayout L;
+  L.n_pad = ceil_div(std::max<int64_t>(N, 1), kTile) * kTile;
+  L.vc = plan_chunk(V);
+  L.fstride = L.vc / 64;
+  L.g_bytes = align_up((size_t)L.n_pad * (size_t)L.vc * dtype_size(dt));
+  L.flag_bytes = align_up((size_t)(L.n_pad / 64) * (size_t)L.fstride);
+  L.total = L.g_bytes + L.flag_bytes;
+  return L;
+}
+size_t fwd_bytes(int64_t N, int64_t V) {
+  return align_up((size_t)plan_splits(N, V) * (size_t)std::max<int64_t>(N, 1) * 8);
+}
+size_t mean_extra_bytes(int64_t N) {
+  return align_up((size_t)ceil_div(std::max<int64_t>(N, 1), 64) * 64 * 8) + kAlign;
+}
+
+cce_status launch_status() {
+  return hipGetLastError() == hipSuccess ? CCE_OK : CCE_ERR_HIP;
+}
+
+int grid_for(int64_t items) { return (int)(ceil_div(items, 8) * 8); }
+
+template <typename T>
+cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, int64_t V,
+                        int64_t D, int64_t ii, float* loss, float* lse, void* ws, int32_t* err,
+                        hipStream_t st) {
+  const int64_t n_split = plan_splits(N, V);
+  const int64_t n_tb = ceil_div(N, kTile), n_vt = ceil_div(V, kTile);
+  const int64_t items = n_tb * n_split;
+  float2* part = (float2*)ws;
+  hipLaunchKernelGGL(k_fwd_lse<T>, dim3(grid_for(items)), dim3(kThreads), 0, st, E, C, (int)N,
+                     (int)V, (int)D, (int)n_split, (int)n_vt, (int)items, part);
+  if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+  hipLaunchKernelGGL(k_fwd_finish<T>, dim3((unsigned)ceil_div(N, 4)), dim3(kThreads), 0, st, E,
+                     C, tgt, (int)N, (int)V, (int)D, (int)n_split, part, ii, loss, lse, err);
+  return launch_status();
+}
+
+template <typename T>
+cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const T* C,
+                         const int64_t* tgt, const float* lse, int64_t N, int64_t V, int64_t D,
+                         int64_t ii, float eps, float* dE, float* dC, void* ws,
+                         int64_t* skip_stats, hipStream_t st, cce_dtype dt) {
+  const BwdLayout L = bwd_layout(N, V, dt);
+  T* G = (T*)ws;
+  uint8_t* flags = (uint8_t*)ws + L.g_bytes;
+  const int64_t n_tb = L.n_pad / kTile, n_dt = ceil_div(D, kTile);
+  constexpr int KS = Traits<T>::kKs;
+  if (skip_stats) {
+    hipLaunchKernelGGL(k_skip_init, dim3(1), dim3(64), 0, st, skip_stats,
+                       ceil_div(N, 64) * ceil_div(V, 64));
+    if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+  }
+  for (int64_t v0 = 0; v0 < V; v0 += L.vc) {
+    const int64_t vc = std::min<int64_t>(L.vc, V - v0);
+    const int64_t n_vtc = ceil_div(vc, kTile);
+    const int64_t kv = ceil_div(vc, KS) * KS;
+    {
+      const int64_t sb = ceil_div(n_tb, 4) * ceil_div(n_vtc, 8);
+      hipLaunchKernelGGL(k_bwd_g<T>, dim3(grid_for(sb * 32)), dim3(kThreads), 0, st, E, C, tgt,
+                         lse, dloss, dstride, (int)N, (int)V, (int)D, (int)v0, (int)vc,
+                         (int)n_tb, (int)n_vtc, G, (int64_t)L.vc, flags, (int)L.fstride, eps, ii,
+                         (unsigned long long*)skip_stats);
+      if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+    }
+    {
+      const int64_t sb = ceil_div(n_vtc, 4) * ceil_div(n_dt, 8);
+      hipLaunchKernelGGL(k_bwd_dc<T>, dim3(grid_for(sb * 32)), dim3(kThreads), 0, st, G,
+                         (int64_t)L.vc, E, (int)D, (int)N, (int)L.n_pad, (int)vc, flags,
+                         (int)L.fstride, (int)n_vtc, (int)n_dt, dC + v0 * D);
+      if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+    }
+    {
+      const int64_t sb = ceil_div(n_tb, 4) * ceil_div(n_dt, 8);
+      hipLaunchKernelGGL(k_bwd_de<T>, dim3(grid_for(sb * 32)), dim3(kThreads), 0, st, G,
+                         (int64_t)L.vc, C + v0 * D, (int)D, (int)N, (int)kv, (int)vc, flags,
+                         (int)L.fstride, (int)n_tb, (int)n_dt, dE, v0 > 0 ? 1 : 0);
+      if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+    }
+  }
+  return CCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cce_status_string(cce_status s) {
+  switch (s) {
+    case CCE_OK: return "CCE_OK";
+    case CCE_ERR_INVALID_ARGUMENT: return "CCE_ERR_INVALID_ARGUMENT";
+    case CCE_ERR_UNSUPPORTED: return "CCE_ERR_UNSUPPORTED";
+    case CCE_ERR_WORKSPACE_TOO_SMALL: return "CCE_ERR_WORKSPACE_TOO_SMALL";
+    case CCE_ERR_HIP: return "CCE_ERR_HIP";
+  }
+  return "CCE_ERR_UNKNOWN";
+}
+
+size_t cce_forward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
+  if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
+  return fwd_bytes(N, V);
+}
+
+size_t cce_backward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
+  if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
+  return bwd_layout(N, V, dt).total;
+}
+
+size_t cce_loss_mean_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
+  if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
+  return fwd_bytes(N, V) + bwd_layout(N, V, dt).total + mean_extra_bytes(N);
+}
+
+int64_t cce_forward_splits(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
+  if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
+  return plan_splits(N, V);
+}
+
+int64_t cce_backward_chunk(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
+  if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
+  return plan_chunk(V);
+}
+
+cce_status cce_forward(const void* E, const void* C, const int64_t* targets, int64_t N,
+                       int64_t V, int64_t D, cce_dtype dt, int64_t ignore_index, float* loss,
+                       float* lse, void* ws, size_t ws_bytes, int32_t* err_flag, void* stream) {
+  if (!sizes_ok(N, V, D, dt)) return CCE_ERR_INVALID_ARGUMENT;
+  if (!sizes_supported(N, V, D)) return CCE_ERR_UNSUPPORTED;
+  if (N == 0) return CCE_OK;
+  if (!E || !C || !targets || !loss || !lse || !ws) return CCE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < fwd_bytes(N, V)) return CCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = (hipStream_t)stream;
+  if (dt == CCE_BF16)
+    return forward_impl<__bf16>((const __bf16*)E, (const __bf16*)C, targets, N, V, D,
+                                ignore_index, loss, lse, ws, err_flag, st);
+  return forward_impl<float>((const float*)E, (const float*)C, targets, N, V, D, ignore_index,
+                             loss, lse, ws, err_flag, st);
+}
+
+cce_status cce_backward(const float* dloss, int64_t dloss_stride, const void* E, const void* C,
+                        const int64_t* targets, const float* lse, int64_t N, int64_t V,
+                        int64_t D, cce_dtype dt, int64_t ignore_index, float filter_eps,
+                        float* dE, float* dC, void* ws, size_t ws_bytes, int64_t* skip_stats,
+                        void* stream) {
+  if (!sizes_ok(N, V, D, dt)) return CCE_ERR_INVALID_ARGUMENT;
+  if (!sizes_supported(N, V, D)) return CCE_ERR_UNSUPPORTED;
+  if (!std::isfinite(filter_eps) || filter_eps < 0.f) return CCE_ERR_INVALID_ARGUMENT;
+  if (dloss_stride != 0 && dloss_stride != 1) return CCE_ERR_INVALID_ARGUMENT;
+  if (N == 0) {
+    // nothing to reduce: dC is still defined (all zero) and so are the statistics
+    if (!dC) return CCE_ERR_INVALID_ARGUMENT;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t n = V * D;
+    hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)std::min<int64_t>(ceil_div(n, 1024), 4096)),
+                       dim3(256), 0, st, dC, n);
+    if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+    if (skip_stats) {
+      hipLaunchKernelGGL(k_skip_init, dim3(1), dim3(64), 0, st, skip_stats, (int64_t)0);
+      if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+    }
+    return CCE_OK;
+  }
+  if (!dloss || !E || !C || !targets || !lse || !dE || !dC || !ws)
+    return CCE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < bwd_layout(N, V, dt).total) return CCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = (hipStream_t)stream;
+  if (dt == CCE_BF16)
+    return backward_impl<__bf16>(dloss, dloss_stride, (const __bf16*)E, (const __bf16*)C,
+                                 targets, lse, N, V, D, ignore_index, filter_eps, dE, dC, ws,
+                                 skip_stats, st, dt);
+  return backward_impl<float>(dloss, dloss_stride, (const float*)E, (const float*)C, targets,
+                              lse, N, V, D, ignore_index, filter_eps, dE, dC, ws, skip_stats,
+                              st, dt);
+}
+
+cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, int64_t N,
+                         int64_t V, int64_t D, cce_dtype dt, int64_t ignore_index,
+                         float filter_eps, float* loss_mean, int64_t* n_valid, float* dE,
+                         float* dC, void* ws, size_t ws_bytes, int32_t* err_flag,
+                         int64_t* skip_stats, void* stream) {
+  if (!sizes_ok(N, V, D, dt)) return CCE_ERR_INVALID_ARGUMENT;
+  if (!sizes_supported(N, V, D)) return CCE_ERR_UNSUPPORTED;
+  if (!std::isfinite(filter_eps) || filter_eps < 0.f) return CCE_ERR_INVALID_ARGUMENT;
+  if (!loss_mean || !dC || !ws) return CCE_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!E || !C || !targets || !dE)) return CCE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < cce_loss_mean_workspace_bytes(N, V, D, dt)) return CCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t fb = fwd_bytes(N, V), bb = bwd_layout(N, V, dt).total;
+  char* base = (char*)ws;
+  char* extra = base + fb + bb;
+  const size_t rows = (size_t)ceil_div(std::max<int64_t>(N, 1), 64) * 64;
+  float* loss = (float*)extra;
+  float* lse = loss + rows;
+  float* dloss = (float*)(extra + align_up(rows * 8));
+  if (N == 0) {
+    hipLaunchKernelGGL(k_mean, dim3(1), dim3(1024), 0, st, (const float*)nullptr,
+                       (const int64_t*)nullptr, 0, ignore_index, loss_mean, dloss, n_valid);
+    if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+    return cce_backward(dloss, 0, E, C, targets, lse, 0, V, D, dt, ignore_index, filter_eps,
+                        dE, dC, base + fb, bb, skip_stats, stream);
+  }
+  cce_status s = cce_forward(E, C, targets, N, V, D, dt, ignore_index, loss, lse, base, fb,
+                             err_flag, stream);
+  if (s != CCE_OK) return s;
+  hipLaunchKernelGGL(k_mean, dim3(1), dim3(1024), 0, st, loss, targets, (int)N, ignore_index,
+                     loss_mean, dloss, n_valid);
+  if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+  return cce_backward(dloss, 0, E, C, targets, lse, N, V, D, dt, ignore_index, filter_eps, dE,
+                      dC, base + fb, bb, skip_stats, stream);
+}
+
+}  // extern "C"

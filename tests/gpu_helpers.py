@@ -1,0 +1,94 @@
+"""Shared helpers of the GPU parity tests (upload, run through the C ABI, compare)."""
+import numpy as np
+import torch
+
+import cce_synth as S
+import linear_cross_entropy_cce_amd as cce
+import oracle
+
+DEV = "cuda:0"
+II = S.IGNORE_INDEX
+EPS = S.FILTER_EPS
+LOSS_TOL = 2e-3      # per-token loss, absolute
+GRAD_TOL = 1e-2      # dE, dC relative Frobenius
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def torch_dtype(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def upload(d, dtype):
+    tdt = torch_dtype(dtype)
+    return (torch.from_numpy(d["E"]).to(DEV, tdt), torch.from_numpy(d["C"]).to(DEV, tdt),
+            torch.from_numpy(np.ascontiguousarray(d["targets"])).to(DEV))
+
+
+def rel(a, b):
+    nb = float(np.linalg.norm(b))
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b)) / (nb if nb > 0 else 1.0)
+
+
+def gpu_run(d, dtype, w, eps, err=False):
+    """Forward + backward through libcce; returns numpy results and the skip statistics."""
+    E, C, t = upload(d, dtype)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    loss, lse = cce.cce_forward(E, C, t, II, err_flag=flag)
+    stats = torch.full((2,), -1, dtype=torch.int64, device=DEV)
+    dl = torch.from_numpy(np.asarray(w, np.float32)).to(DEV)
+    dE, dC = cce.cce_backward(dl, E, C, t, lse, II, eps, skip_stats=stats)
+    torch.cuda.synchronize()
+    out = dict(loss=loss.cpu().numpy(), lse=lse.cpu().numpy(), dE=dE.cpu().numpy(),
+               dC=dC.cpu().numpy(), skipped=int(stats[0]), total=int(stats[1]),
+               err=int(flag.item()))
+    return out
+
+
+def borderline_blocks(E, C, t, eps, bn=64, bv=64, rel_band=1e-3):
+    """Blocks whose decision the rounding of fp32 vs fp64 may flip: no target inside and a
+    block max of the softmax within rel_band of eps (computed from the oracle's values)."""
+    if eps <= 0:
+        return 0
+    _, lse = oracle.forward(E, C, t, II)
+    N, V = E.shape[0], C.shape[0]
+    count = 0
+    for n0 in range(0, N, bn):
+        rows = np.arange(n0, min(N, n0 + bn))
+        valid = t[rows] != II
+        if not valid.any():
+            continue
+        P = np.exp(oracle.logits(E[rows[valid]], C) - lse[rows[valid], None])
+        for v0 in range(0, V, bv):
+            tv = t[rows[valid]]
+            if ((tv >= v0) & (tv < v0 + bv)).any():
+                continue
+            m = P[:, v0:v0 + bv].max()
+            if abs(m - eps) <= rel_band * eps:
+                count += 1
+    return count
+
+
+def check_against_oracle(d, dtype, w, eps, name, grad_tol=GRAD_TOL, loss_tol=LOSS_TOL):
+    log(f"[{name}] N={d['E'].shape[0]} D={d['E'].shape[1]} V={d['C'].shape[0]} {dtype} eps={eps}")
+    g = gpu_run(d, dtype, w, eps)
+    E, C, t = d["E"], d["C"], d["targets"]
+    loss, lse = oracle.forward(E, C, t, II)
+    dE, dC, (sk, tot) = oracle.backward(E, C, t, w, II, filter_eps=eps)
+    assert np.abs(g["loss"] - loss).max() <= loss_tol, np.abs(g["loss"] - loss).max()
+    assert np.abs(g["lse"] - lse).max() <= loss_tol
+    assert np.all(g["loss"][t == II] == 0.0)
+    assert rel(g["dE"], dE) <= grad_tol, rel(g["dE"], dE)
+    assert rel(g["dC"], dC) <= grad_tol, rel(g["dC"], dC)
+    assert np.all(g["dE"][t == II] == 0.0)
+    assert g["total"] == tot
+    border = borderline_blocks(E, C, t, eps)
+    assert abs(g["skipped"] - sk) <= border, (g["skipped"], sk, border)
+    if eps > 0:   # the filtered result is also within tolerance of the unfiltered oracle
+        dE0, dC0, _ = oracle.backward(E, C, t, w, II)
+        assert rel(g["dE"], dE0) <= GRAD_TOL and rel(g["dC"], dC0) <= GRAD_TOL
+    log(f"[{name}] ok: loss {np.abs(g['loss'] - loss).max():.2e} dE {rel(g['dE'], dE):.2e} "
+        f"dC {rel(g['dC'], dC):.2e} skipped {g['skipped']}/{g['total']} (oracle {sk})")
+    return g

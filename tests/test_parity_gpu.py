@@ -1,0 +1,174 @@
+"""GPU parity: libcce (HIP, gfx950) against the float64 CPU oracle, element by element, on
+seeded inputs that span several 256 x 256 tiles with ragged tails, several backward vocabulary
+chunks, and the degenerate cases of the method."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import cce_synth as S
+import linear_cross_entropy_cce_amd as cce
+import oracle
+from gpu_helpers import (DEV, EPS, GRAD_TOL, II, LOSS_TOL, check_against_oracle, gpu_run, log,
+                         rel, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_workload_fp32():
+    w = S.WORKLOADS["tiny"]
+    d = S.make_inputs(w)
+    g = check_against_oracle(d, "f32", S.dloss_weights(1, w.N), 0.0, "tiny")
+    ref, _ = oracle.forward(d["E"], d["C"], d["targets"], II)
+    assert np.abs(g["loss"] - ref).max() < 1e-4    # fp32 MFMA: far inside the tolerance
+
+
+SMALL = [
+    # name, N, D, V, dtype, c_scale, zipf, ignore_frac, seed
+    ("bf16_ragged", 300, 136, 1100, "bf16", 3.0, 1.1, 0.1, 11),
+    ("bf16_tiles", 512, 256, 2048, "bf16", 3.0, 1.1, 0.0, 12),
+    ("f32_ragged", 130, 36, 777, "f32", 2.0, None, 0.1, 13),
+    ("bf16_k_tail", 257, 72, 300, "bf16", 2.0, 1.0, 0.2, 14),
+    ("bf16_one_token", 1, 64, 300, "bf16", 3.0, None, 0.0, 15),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+@pytest.mark.parametrize("eps", [0.0, EPS])
+def test_small_cases(case, eps):
+    name, N, D, V, dt, cs, z, ig, seed = case
+    d = S.small_case(N, D, V, dt, seed, cs, z, ig)
+    check_against_oracle(d, dt, S.dloss_weights(seed, N), eps, name)
+
+
+def test_several_vocabulary_chunks():
+    """V = 20000 spans three backward chunks (8192 + 8192 + a ragged 3616)."""
+    d = S.small_case(300, 72, 20000, "bf16", 21, 3.0, 1.1, 0.05)
+    assert cce.backward_chunk(300, 20000, 72, torch.bfloat16) == 8192
+    check_against_oracle(d, "bf16", S.dloss_weights(21, 300), EPS, "chunks")
+
+
+def test_sparse_softmax_skips_blocks():
+    w = S.Workload("sparse_small", 320, 128, 3000, "bf16", 12.0, 1.2, boost_frac=0.05, seed=3)
+    d = S.make_inputs(w)
+    g = check_against_oracle(d, "bf16", S.dloss_weights(3, 320), EPS, "sparse_small")
+    assert g["skipped"] > 0
+
+
+def test_far_vocabulary_blocks_are_skipped_exactly():
+    """Vocabulary blocks 1 and 3 (64 wide) get logits near -200 for every token: each of
+    their (token block, vocabulary block) pairs must be skipped and nothing else."""
+    N, V, D = 150, 320, 64
+    g = np.random.default_rng(31)
+    E = S.bf16_round(np.concatenate([np.full((N, 1), 10.0), 0.1 * g.standard_normal((N, D - 1))],
+                                    axis=1).astype(np.float32))
+    C = 0.05 * g.standard_normal((V, D)).astype(np.float32)
+    far = np.r_[64:128, 192:256]
+    C[far, 0] = -20.0
+    C = S.bf16_round(C)
+    t = g.choice(np.setdiff1d(np.arange(V), far), size=N).astype(np.int64)
+    d = {"E": E, "C": C, "targets": t}
+    out = check_against_oracle(d, "bf16", np.ones(N, np.float32), EPS, "far_blocks")
+    assert (out["skipped"], out["total"]) == (3 * 2, 3 * 5)
+
+
+def test_zero_embeddings_give_log_v():
+    N, V, D = 70, 1000, 64
+    d = S.small_case(N, D, V, "bf16", 41, 3.0, 1.1, 0.0)
+    d["E"][:] = 0.0
+    out = gpu_run(d, "bf16", np.ones(N, np.float32), 0.0)
+    assert np.abs(out["loss"] - math.log(V)).max() < 1e-5
+    assert np.abs(out["dC"]).max() == 0.0
+    check_against_oracle(d, "bf16", np.ones(N, np.float32), 0.0, "zero_E")
+
+
+@pytest.mark.parametrize("V", [1, 2])
+def test_tiny_vocabularies(V):
+    d = S.small_case(70, 16, V, "bf16", 42 + V, 3.0, None, 0.1)
+    g = check_against_oracle(d, "bf16", S.dloss_weights(7, 70), 0.0, f"V{V}")
+    if V == 1:
+        assert np.abs(g["loss"]).max() < 1e-6
+
+
+def test_all_tokens_ignored():
+    d = S.small_case(100, 64, 500, "bf16", 51, 3.0, 1.1, 0.0)
+    d["targets"][:] = II
+    out = gpu_run(d, "bf16", np.ones(100, np.float32), EPS)
+    assert np.all(out["loss"] == 0.0) and np.all(out["dE"] == 0.0) and np.all(out["dC"] == 0.0)
+    _, lse = oracle.forward(d["E"], d["C"], d["targets"], II)
+    assert np.abs(out["lse"] - lse).max() < LOSS_TOL
+    assert out["skipped"] == out["total"]   # no valid row makes any block significant
+
+
+def test_dominant_logit_stays_finite():
+    N, V, D = 64, 512, 64
+    E = np.zeros((N, D), np.float32)
+    E[np.arange(N), np.arange(N) % D] = 32.0
+    C = np.zeros((V, D), np.float32)
+    t = (np.arange(N) * 7 % V).astype(np.int64)
+    C[t, np.arange(N) % D] = 32.0       # target logit 1024 (bf16 exact), the rest 0 or 1024
+    d = {"E": E, "C": C, "targets": t}
+    out = gpu_run(d, "bf16", np.ones(N, np.float32), EPS)
+    assert np.all(np.isfinite(out["loss"])) and np.all(np.isfinite(out["dE"]))
+    check_against_oracle(d, "bf16", np.ones(N, np.float32), EPS, "dominant")
+
+
+def test_invalid_target_sets_flag_and_nan():
+    d = S.small_case(40, 64, 100, "bf16", 61, 3.0, None, 0.0)
+    d["targets"][5] = 100
+    out = gpu_run(d, "bf16", np.ones(40, np.float32), 0.0)
+    assert out["err"] == 1 and np.isnan(out["loss"][5])
+    assert np.all(np.isfinite(np.delete(out["loss"], 5)))
+
+
+def test_empty_batch():
+    E = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    C = torch.randn((300, 64), device=DEV).to(torch.bfloat16)
+    t = torch.zeros(0, dtype=torch.int64, device=DEV)
+    loss, lse = cce.cce_forward(E, C, t)
+    dC = torch.full((300, 64), 7.0, device=DEV)
+    stats = torch.full((2,), -1, dtype=torch.int64, device=DEV)
+    dE, dC = cce.cce_backward(torch.ones(0, device=DEV), E, C, t, lse, dC=dC, skip_stats=stats)
+    torch.cuda.synchronize()
+    assert loss.numel() == 0 and dE.numel() == 0
+    assert float(dC.abs().max()) == 0.0 and stats.tolist() == [0, 0]
+
+
+def test_scalar_dloss_equals_vector():
+    d = S.small_case(200, 64, 900, "bf16", 71, 3.0, 1.1, 0.1)
+    E, C, t = upload(d, "bf16")
+    _, lse = cce.cce_forward(E, C, t)
+    a = cce.cce_backward(torch.full((1,), 0.37, device=DEV), E, C, t, lse, filter_eps=EPS)
+    b = cce.cce_backward(torch.full((200,), 0.37, device=DEV), E, C, t, lse, filter_eps=EPS)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_runs_are_bitwise_deterministic():
+    d = S.small_case(520, 128, 9000, "bf16", 81, 3.0, 1.1, 0.1)
+    w = S.dloss_weights(81, 520)
+    a = gpu_run(d, "bf16", w, EPS)
+    b = gpu_run(d, "bf16", w, EPS)
+    for k in ("loss", "lse", "dE", "dC"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_loss_mean_matches_oracle():
+    d = S.small_case(333, 72, 1500, "bf16", 91, 3.0, 1.1, 0.25)
+    E, C, t = upload(d, "bf16")
+    mean, nv, dE, dC = cce.cce_loss_mean(E, C, t, II, EPS)
+    torch.cuda.synchronize()
+    m, rE, rC, n = oracle.loss_mean(d["E"], d["C"], d["targets"], II, EPS)
+    assert int(nv.item()) == n
+    assert abs(float(mean.item()) - m) <= LOSS_TOL
+    assert rel(dE.cpu().numpy(), rE) <= GRAD_TOL and rel(dC.cpu().numpy(), rC) <= GRAD_TOL
+
+
+def test_loss_mean_all_ignored_is_zero():
+    d = S.small_case(64, 64, 300, "bf16", 92, 3.0, 1.1, 0.0)
+    d["targets"][:] = II
+    E, C, t = upload(d, "bf16")
+    mean, nv, dE, dC = cce.cce_loss_mean(E, C, t, II, 0.0)
+    torch.cuda.synchronize()
+    assert float(mean.item()) == 0.0 and int(nv.item()) == 0
+    assert float(dE.abs().max()) == 0.0 and float(dC.abs().max()) == 0.0
