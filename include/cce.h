@@ -113,6 +113,27 @@ cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, i
 int64_t cce_forward_splits(int64_t N, int64_t V, int64_t D, cce_dtype dtype);
 int64_t cce_backward_chunk(int64_t N, int64_t V, int64_t D, cce_dtype dtype);
 
+/* Kernel kinds, for per-kernel timing. */
+typedef enum {
+  CCE_KERNEL_FWD_LSE = 0,     /* logit tiles + online log-sum-exp partials    (2 N V D flops) */
+  CCE_KERNEL_FWD_FINISH = 1,  /* partial merge, target gather-dot, loss                       */
+  CCE_KERNEL_BWD_G = 2,       /* logit recompute, softmax - onehot, filter    (2 N Vc D / chunk) */
+  CCE_KERNEL_BWD_DC = 3,      /* dC chunk = G^T E                              (2 N Vc D / chunk) */
+  CCE_KERNEL_BWD_DE = 4,      /* dE += G C chunk                               (2 N Vc D / chunk) */
+  CCE_KERNEL_AUX = 5,         /* small helpers (statistics init, mean, zero fill)               */
+  CCE_KERNEL_KINDS = 6
+} cce_kernel_kind;
+
+/* Benchmark timing hook (host only, not thread safe, process-wide).  cce_timing_begin starts
+ * recording a HIP event pair around each of the next launches (at most max_launches) of every
+ * kernel kind whose bit is set in kind_mask, on the stream the kernel is launched on.
+ * cce_timing_end waits for the recorded events, writes the summed durations in milliseconds
+ * and the launch counts per kind into ms[CCE_KERNEL_KINDS] and launches[CCE_KERNEL_KINDS]
+ * (host arrays), releases the events and stops recording.  Returns CCE_ERR_HIP if an event
+ * call fails, CCE_ERR_INVALID_ARGUMENT for max_launches < 1 or NULL outputs. */
+cce_status cce_timing_begin(uint32_t kind_mask, int32_t max_launches);
+cce_status cce_timing_end(float* ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -4,10 +4,11 @@ The classifier-head cross-entropy loss, lse_v(E C_v^T) - E C_target^T, and its g
 dC, computed by hand-written HIP kernels without writing the N x V logits to device memory
 (the Cut Cross-Entropy abstract, taxoreview.com page dblp:393/3562, sentences 4-6 and 9).
 """
-from ._lib import (CCEError, LIB_PATH, backward_chunk, backward_workspace_bytes, cce_backward,
-                   cce_forward, cce_loss_mean, forward_splits, forward_workspace_bytes, lib,
-                   loss_mean_workspace_bytes)
+from ._lib import (KERNEL_KINDS, CCEError, LIB_PATH, backward_chunk, backward_workspace_bytes,
+                   cce_backward, cce_forward, cce_loss_mean, forward_splits,
+                   forward_workspace_bytes, lib, loss_mean_workspace_bytes, timing_begin,
+                   timing_end)
 
 __all__ = ["CCEError", "LIB_PATH", "backward_chunk", "backward_workspace_bytes", "cce_backward",
            "cce_forward", "cce_loss_mean", "forward_splits", "forward_workspace_bytes", "lib",
-           "loss_mean_workspace_bytes"]
+           "loss_mean_workspace_bytes", "KERNEL_KINDS", "timing_begin", "timing_end"]

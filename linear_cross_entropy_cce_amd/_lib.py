@@ -37,7 +37,11 @@ SIGNATURES = {
                             _i64, _f32, _c_ptr, _c_ptr, _c_ptr, _sz, _c_ptr, _c_ptr]),
     "cce_loss_mean": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _f32, _c_ptr,
                              _c_ptr, _c_ptr, _c_ptr, _c_ptr, _sz, _c_ptr, _c_ptr, _c_ptr]),
+    "cce_timing_begin": (_i32, [ctypes.c_uint32, ctypes.c_int32]),
+    "cce_timing_end": (_i32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int64)]),
 }
+
+KERNEL_KINDS = ("fwd_lse", "fwd_finish", "bwd_g", "bwd_dc", "bwd_de", "aux")
 
 
 class CCEError(RuntimeError):
@@ -176,3 +180,20 @@ def cce_loss_mean(E, C, targets, ignore_index: int = -100, filter_eps: float = 0
         _ptr(mean), _ptr(n_valid), _ptr(dE), _ptr(dC), _ptr(ws), ws.numel() * ws.element_size(),
         _ptr(err_flag), _ptr(skip_stats), _stream(stream)))
     return mean, n_valid, dE, dC
+
+
+def timing_begin(kinds=KERNEL_KINDS, max_launches: int = 100000) -> None:
+    """Starts recording HIP event pairs around launches of the given kernel kinds."""
+    mask = 0
+    for k in kinds:
+        mask |= 1 << KERNEL_KINDS.index(k)
+    _check("cce_timing_begin", lib().cce_timing_begin(mask, max_launches))
+
+
+def timing_end() -> dict:
+    """Stops recording; returns {kind: (total_ms, launches)} for kinds that ran."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_float * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check("cce_timing_end", lib().cce_timing_end(ms, cnt))
+    return {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(KERNEL_KINDS) if cnt[i]}

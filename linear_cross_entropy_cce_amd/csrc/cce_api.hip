@@ -101,6 +101,34 @@ cce_status launch_status() {
   return hipGetLastError() == hipSuccess ? CCE_OK : CCE_ERR_HIP;
 }
 
+// Benchmark timing hook: event pairs around launches of the selected kernel kinds.
+struct Timing {
+  bool on = false;
+  uint32_t mask = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;   // 2 per launch slot
+  std::vector<int> kind;
+};
+Timing g_timing;
+
+struct TimedLaunch {
+  bool rec = false;
+  hipStream_t st;
+  TimedLaunch(int kind, hipStream_t s) : st(s) {
+    Timing& T = g_timing;
+    if (T.on && ((T.mask >> kind) & 1u) && T.used < (int)T.kind.size()) {
+      rec = hipEventRecord(T.ev[2 * T.used], st) == hipSuccess;
+      if (rec) T.kind[T.used] = kind;
+    }
+  }
+  ~TimedLaunch() {
+    if (rec) {
+      Timing& T = g_timing;
+      if (hipEventRecord(T.ev[2 * T.used + 1], st) == hipSuccess) ++T.used;
+    }
+  }
+};
+
 int grid_for(int64_t items) { return (int)(ceil_div(items, 8) * 8); }
 
 template <typename T>
@@ -111,9 +139,13 @@ cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, i
   const int64_t n_tb = ceil_div(N, kTile), n_vt = ceil_div(V, kTile);
   const int64_t items = n_tb * n_split;
   float2* part = (float2*)ws;
+  {
+  TimedLaunch tl(CCE_KERNEL_FWD_LSE, st);
   hipLaunchKernelGGL(k_fwd_lse<T>, dim3(grid_for(items)), dim3(kThreads), 0, st, E, C, (int)N,
                      (int)V, (int)D, (int)n_split, (int)n_vt, (int)items, part);
+  }
   if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+  TimedLaunch tl(CCE_KERNEL_FWD_FINISH, st);
   hipLaunchKernelGGL(k_fwd_finish<T>, dim3((unsigned)ceil_div(N, 4)), dim3(kThreads), 0, st, E,
                      C, tgt, (int)N, (int)V, (int)D, (int)n_split, part, ii, loss, lse, err);
   return launch_status();
@@ -130,6 +162,7 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
   const int64_t n_tb = L.n_pad / kTile, n_dt = ceil_div(D, kTile);
   constexpr int KS = Traits<T>::kKs;
   if (skip_stats) {
+    TimedLaunch tl(CCE_KERNEL_AUX, st);
     hipLaunchKernelGGL(k_skip_init, dim3(1), dim3(64), 0, st, skip_stats,
                        ceil_div(N, 64) * ceil_div(V, 64));
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
@@ -140,6 +173,7 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
     const int64_t kv = ceil_div(vc, KS) * KS;
     {
       const int64_t sb = ceil_div(n_tb, 4) * ceil_div(n_vtc, 8);
+      TimedLaunch tl(CCE_KERNEL_BWD_G, st);
       hipLaunchKernelGGL(k_bwd_g<T>, dim3(grid_for(sb * 32)), dim3(kThreads), 0, st, E, C, tgt,
                          lse, dloss, dstride, (int)N, (int)V, (int)D, (int)v0, (int)vc,
                          (int)n_tb, (int)n_vtc, G, (int64_t)L.vc, flags, (int)L.fstride, eps, ii,
@@ -148,6 +182,7 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
     }
     {
       const int64_t sb = ceil_div(n_vtc, 4) * ceil_div(n_dt, 8);
+      TimedLaunch tl(CCE_KERNEL_BWD_DC, st);
       hipLaunchKernelGGL(k_bwd_dc<T>, dim3(grid_for(sb * 32)), dim3(kThreads), 0, st, G,
                          (int64_t)L.vc, E, (int)D, (int)N, (int)L.n_pad, (int)vc, flags,
                          (int)L.fstride, (int)n_vtc, (int)n_dt, dC + v0 * D);
@@ -155,6 +190,7 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
     }
     {
       const int64_t sb = ceil_div(n_tb, 4) * ceil_div(n_dt, 8);
+      TimedLaunch tl(CCE_KERNEL_BWD_DE, st);
       hipLaunchKernelGGL(k_bwd_de<T>, dim3(grid_for(sb * 32)), dim3(kThreads), 0, st, G,
                          (int64_t)L.vc, C + v0 * D, (int)D, (int)N, (int)kv, (int)vc, flags,
                          (int)L.fstride, (int)n_tb, (int)n_dt, dE, v0 > 0 ? 1 : 0);
@@ -285,11 +321,48 @@ cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, i
   cce_status s = cce_forward(E, C, targets, N, V, D, dt, ignore_index, loss, lse, base, fb,
                              err_flag, stream);
   if (s != CCE_OK) return s;
-  hipLaunchKernelGGL(k_mean, dim3(1), dim3(1024), 0, st, loss, targets, (int)N, ignore_index,
-                     loss_mean, dloss, n_valid);
+  {
+    TimedLaunch tl(CCE_KERNEL_AUX, st);
+    hipLaunchKernelGGL(k_mean, dim3(1), dim3(1024), 0, st, loss, targets, (int)N, ignore_index,
+                       loss_mean, dloss, n_valid);
+  }
   if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   return cce_backward(dloss, 0, E, C, targets, lse, N, V, D, dt, ignore_index, filter_eps, dE,
                       dC, base + fb, bb, skip_stats, stream);
+}
+
+cce_status cce_timing_begin(uint32_t kind_mask, int32_t max_launches) {
+  if (max_launches < 1) return CCE_ERR_INVALID_ARGUMENT;
+  Timing& T = g_timing;
+  for (hipEvent_t e : T.ev) (void)hipEventDestroy(e);
+  T = Timing();
+  T.ev.resize(2 * (size_t)max_launches);
+  for (auto& e : T.ev)
+    if (hipEventCreate(&e) != hipSuccess) return CCE_ERR_HIP;
+  T.kind.assign((size_t)max_launches, 0);
+  T.mask = kind_mask;
+  T.on = true;
+  return CCE_OK;
+}
+
+cce_status cce_timing_end(float* ms, int64_t* launches) {
+  if (!ms || !launches) return CCE_ERR_INVALID_ARGUMENT;
+  Timing& T = g_timing;
+  for (int k = 0; k < CCE_KERNEL_KINDS; ++k) { ms[k] = 0.f; launches[k] = 0; }
+  cce_status st = CCE_OK;
+  for (int i = 0; i < T.used; ++i) {
+    float t = 0.f;
+    if (hipEventSynchronize(T.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&t, T.ev[2 * i], T.ev[2 * i + 1]) != hipSuccess) {
+      st = CCE_ERR_HIP;
+      continue;
+    }
+    ms[T.kind[i]] += t;
+    launches[T.kind[i]] += 1;
+  }
+  for (hipEvent_t e : T.ev) (void)hipEventDestroy(e);
+  T = Timing();
+  return st;
 }
 
 }  // extern "C"
