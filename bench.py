@@ -73,6 +73,19 @@ def cpu_baseline(d, w, n_tokens: int) -> dict:
                       f"contribution over all V={w.V}), {dt:.1f} s"}
 
 
+def copy_calibration() -> int:
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,7 +96,12 @@ def main() -> int:
                     help="override the workload's gradient filter threshold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (3 times): the reference kernel "
+                         "for scaling the HBM byte counters of a profiler")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -158,8 +176,10 @@ def main() -> int:
     # dominant kernel: the kind with the largest time per step
     per_step = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps}
                 for k, v in kernels.items()}
-    flops_per_step = {"fwd_lse": flop_fwd, "bwd_g": 2.0 * N * V * D, "bwd_dc": 2.0 * N * V * D,
-                      "bwd_de": 2.0 * N * V * D}
+    vc0 = min(cce.backward_chunk(N, V, D, tdt), V)      # width of the first chunk
+    flops_per_step = {"fwd_lse": flop_fwd,
+                      "bwd_g": 2.0 * N * vc0 * D,               # recompute of the first chunk
+                      "bwd_fused": 4.0 * N * V * D + 2.0 * N * (V - vc0) * D}
     dom = max((k for k in per_step if k in flops_per_step), key=lambda k: per_step[k]["ms_per_step"])
     dom_ms_launch = kernels[dom][0] / kernels[dom][1]
     dom_flop_launch = flops_per_step[dom] / per_step[dom]["launches_per_step"]

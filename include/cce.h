@@ -57,8 +57,8 @@ const char* cce_status_string(cce_status s);
  * Pure host functions.  Each formula is linear in N for fixed V and D (no N*V term):
  *   forward : splits * N * 8 bytes, splits <= 256 vocabulary ranges (an on-chip LSE partial
  *             per token and range), rounded to 256 bytes;
- *   backward: roundup(N,256) * Vc * sizeof(dtype) for one vocabulary chunk of the
- *             softmax-gradient tile store (Vc <= 8192 columns), plus its 64x64 block flags;
+ *   backward: 2 * roundup(N,256) * Vc * sizeof(dtype): the softmax-gradient tile store of two
+ *             vocabulary chunks in flight (Vc <= 8192 columns), plus their 64x64 block flags;
  *   mean    : forward + backward + 8 * roundup(N,64) + 256.
  * Returns 0 for invalid sizes. */
 size_t cce_forward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dtype);
@@ -115,13 +115,13 @@ int64_t cce_backward_chunk(int64_t N, int64_t V, int64_t D, cce_dtype dtype);
 
 /* Kernel kinds, for per-kernel timing. */
 typedef enum {
-  CCE_KERNEL_FWD_LSE = 0,     /* logit tiles + online log-sum-exp partials    (2 N V D flops) */
-  CCE_KERNEL_FWD_FINISH = 1,  /* partial merge, target gather-dot, loss                       */
-  CCE_KERNEL_BWD_G = 2,       /* logit recompute, softmax - onehot, filter    (2 N Vc D / chunk) */
-  CCE_KERNEL_BWD_DC = 3,      /* dC chunk = G^T E                              (2 N Vc D / chunk) */
-  CCE_KERNEL_BWD_DE = 4,      /* dE += G C chunk                               (2 N Vc D / chunk) */
-  CCE_KERNEL_AUX = 5,         /* small helpers (statistics init, mean, zero fill)               */
-  CCE_KERNEL_KINDS = 6
+  CCE_KERNEL_FWD_LSE = 0,     /* logit tiles + online log-sum-exp partials     (2 N V D flops)   */
+  CCE_KERNEL_FWD_FINISH = 1,  /* partial merge, target gather-dot, loss                          */
+  CCE_KERNEL_BWD_G = 2,       /* logit recompute, softmax - onehot, filter of the first chunk    */
+  CCE_KERNEL_BWD_FUSED = 3,   /* per chunk c: dE += G C and dC = G^T E of chunk c (4 N Vc D)
+                                 with the recompute of chunk c + 1                (2 N Vc' D)  */
+  CCE_KERNEL_AUX = 4,         /* small helpers (statistics init, mean, zero fill)                */
+  CCE_KERNEL_KINDS = 5
 } cce_kernel_kind;
 
 /* Benchmark timing hook (host only, not thread safe, process-wide).  cce_timing_begin starts

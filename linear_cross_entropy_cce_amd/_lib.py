@@ -41,7 +41,7 @@ SIGNATURES = {
     "cce_timing_end": (_i32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int64)]),
 }
 
-KERNEL_KINDS = ("fwd_lse", "fwd_finish", "bwd_g", "bwd_dc", "bwd_de", "aux")
+KERNEL_KINDS = ("fwd_lse", "fwd_finish", "bwd_g", "bwd_fused", "aux")
 
 
 class CCEError(RuntimeError):

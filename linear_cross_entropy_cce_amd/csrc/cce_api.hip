@@ -14,6 +14,13 @@
 #include <vector>
 
 #include "cce.h"
+
+#ifndef CCE_KB
+#define CCE_KB 128
+#endif
+#ifndef CCE_NST
+#define CCE_NST 2
+#endif
 #include "cce_kernels.hpp"
 
 namespace {
@@ -23,6 +30,11 @@ using namespace cce;
 constexpr int64_t kMaxRows = int64_t(1) << 24;
 constexpr int64_t kMaxD = 65536;
 constexpr int kAssumedCUs = 256;  // MI355X; only shapes the launch plan, never correctness
+
+// Pipeline shape of every MFMA kernel: KB bytes of K per operand row and stage, NST stages in
+// flight (LDS: NST x 2 x 256 x KB bytes).
+constexpr int kKB = CCE_KB;
+constexpr int kNST = CCE_NST;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -87,7 +99,7 @@ BwdLayout bwd_layout(int64_t N, int64_t V, cce_dtype dt) {
   L.fstride = L.vc / 64;
   L.g_bytes = align_up((size_t)L.n_pad * (size_t)L.vc * dtype_size(dt));
   L.flag_bytes = align_up((size_t)(L.n_pad / 64) * (size_t)L.fstride);
-  L.total = L.g_bytes + L.flag_bytes;
+  L.total = 2 * (L.g_bytes + L.flag_bytes);   // two chunks in flight: c and c + 1
   return L;
 }
 size_t fwd_bytes(int64_t N, int64_t V) {
@@ -141,7 +153,7 @@ cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, i
   float2* part = (float2*)ws;
   {
   TimedLaunch tl(CCE_KERNEL_FWD_LSE, st);
-  hipLaunchKernelGGL(k_fwd_lse<T>, dim3(grid_for(items)), dim3(kThreads), 0, st, E, C, (int)N,
+  hipLaunchKernelGGL((k_fwd_lse<T, kKB, kNST>), dim3(grid_for(items)), dim3(kThreads), 0, st, E, C, (int)N,
                      (int)V, (int)D, (int)n_split, (int)n_vt, (int)items, part);
   }
   if (launch_status() != CCE_OK) return CCE_ERR_HIP;
@@ -157,45 +169,51 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
                          int64_t ii, float eps, float* dE, float* dC, void* ws,
                          int64_t* skip_stats, hipStream_t st, cce_dtype dt) {
   const BwdLayout L = bwd_layout(N, V, dt);
-  T* G = (T*)ws;
-  uint8_t* flags = (uint8_t*)ws + L.g_bytes;
   const int64_t n_tb = L.n_pad / kTile, n_dt = ceil_div(D, kTile);
-  constexpr int KS = Traits<T>::kKs;
+  const int64_t n_chunks = ceil_div(V, L.vc);
   if (skip_stats) {
     TimedLaunch tl(CCE_KERNEL_AUX, st);
     hipLaunchKernelGGL(k_skip_init, dim3(1), dim3(64), 0, st, skip_stats,
                        ceil_div(N, 64) * ceil_div(V, 64));
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   }
-  for (int64_t v0 = 0; v0 < V; v0 += L.vc) {
-    const int64_t vc = std::min<int64_t>(L.vc, V - v0);
-    const int64_t n_vtc = ceil_div(vc, kTile);
-    const int64_t kv = ceil_div(vc, KS) * KS;
-    {
-      const int64_t sb = ceil_div(n_tb, 4) * ceil_div(n_vtc, 8);
-      TimedLaunch tl(CCE_KERNEL_BWD_G, st);
-      hipLaunchKernelGGL(k_bwd_g<T>, dim3(grid_for(sb * 32)), dim3(kThreads), 0, st, E, C, tgt,
-                         lse, dloss, dstride, (int)N, (int)V, (int)D, (int)v0, (int)vc,
-                         (int)n_tb, (int)n_vtc, G, (int64_t)L.vc, flags, (int)L.fstride, eps, ii,
-                         (unsigned long long*)skip_stats);
-      if (launch_status() != CCE_OK) return CCE_ERR_HIP;
-    }
-    {
-      const int64_t sb = ceil_div(n_vtc, 4) * ceil_div(n_dt, 8);
-      TimedLaunch tl(CCE_KERNEL_BWD_DC, st);
-      hipLaunchKernelGGL(k_bwd_dc<T>, dim3(grid_for(sb * 32)), dim3(kThreads), 0, st, G,
-                         (int64_t)L.vc, E, (int)D, (int)N, (int)L.n_pad, (int)vc, flags,
-                         (int)L.fstride, (int)n_vtc, (int)n_dt, dC + v0 * D);
-      if (launch_status() != CCE_OK) return CCE_ERR_HIP;
-    }
-    {
-      const int64_t sb = ceil_div(n_tb, 4) * ceil_div(n_dt, 8);
-      TimedLaunch tl(CCE_KERNEL_BWD_DE, st);
-      hipLaunchKernelGGL(k_bwd_de<T>, dim3(grid_for(sb * 32)), dim3(kThreads), 0, st, G,
-                         (int64_t)L.vc, C + v0 * D, (int)D, (int)N, (int)kv, (int)vc, flags,
-                         (int)L.fstride, (int)n_tb, (int)n_dt, dE, v0 > 0 ? 1 : 0);
-      if (launch_status() != CCE_OK) return CCE_ERR_HIP;
-    }
+  // chunk c uses G / flag buffer c % 2
+  auto args = [&](int64_t c) {
+    BwdArgs<T> A;
+    const int buf = (int)(c & 1);
+    A.E = E; A.C = C; A.tgt = tgt; A.lse = lse; A.dloss = dloss; A.dstride = dstride;
+    A.N = (int)N; A.V = (int)V; A.D = (int)D; A.n_pad = (int)L.n_pad;
+    A.v0 = (int)(c * L.vc);
+    A.vc = (int)std::min<int64_t>(L.vc, V - c * L.vc);
+    A.n_tb = (int)n_tb; A.n_vtc = (int)ceil_div(A.vc, kTile); A.n_dt = (int)n_dt;
+    A.G = (T*)((char*)ws + buf * L.g_bytes);
+    A.ldg = L.vc;
+    A.flags = (uint8_t*)ws + 2 * L.g_bytes + buf * L.flag_bytes;
+    A.fstride = (int)L.fstride;
+    A.eps = eps; A.ignore_index = ii;
+    A.skip_count = (unsigned long long*)skip_stats;
+    A.dE = dE; A.dC = dC;
+    A.accumulate = c > 0 ? 1 : 0;
+    return A;
+  };
+  {
+    const BwdArgs<T> A0 = args(0);
+    TimedLaunch tl(CCE_KERNEL_BWD_G, st);
+    hipLaunchKernelGGL((k_bwd_g<T, kKB, kNST>), dim3(grid_for(bwd_items(A0.n_tb, A0.n_vtc))),
+                       dim3(kThreads), 0, st, A0);
+    if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+  }
+  for (int64_t c = 0; c < n_chunks; ++c) {
+    const BwdArgs<T> A = args(c);
+    const bool more = c + 1 < n_chunks;
+    const BwdArgs<T> Nx = more ? args(c + 1) : A;
+    const int r_de = grid_for(bwd_items(A.n_tb, A.n_dt));
+    const int r_dc = grid_for(bwd_items(A.n_vtc, A.n_dt));
+    const int r_g = more ? grid_for(bwd_items(Nx.n_tb, Nx.n_vtc)) : 0;
+    TimedLaunch tl(CCE_KERNEL_BWD_FUSED, st);
+    hipLaunchKernelGGL((k_bwd_fused<T, kKB, kNST>), dim3(r_de + r_dc + r_g), dim3(kThreads), 0,
+                       st, A, Nx, r_de, r_dc);
+    if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   }
   return CCE_OK;
 }

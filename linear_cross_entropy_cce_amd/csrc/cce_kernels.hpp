@@ -20,28 +20,55 @@
 
 namespace cce {
 
+// NST double-operand stage buffers as distinct LDS objects (unused ones shrink to 16 bytes).
+#define CCE_STAGE_BUFFERS(KB, NST, B)                                                          \
+  __shared__ __attribute__((aligned(1024))) char sA0_[Geo<KB>::kOpBytes];                     \
+  __shared__ __attribute__((aligned(1024))) char sB0_[Geo<KB>::kOpBytes];                     \
+  __shared__ __attribute__((aligned(1024))) char sA1_[Geo<KB>::kOpBytes];                     \
+  __shared__ __attribute__((aligned(1024))) char sB1_[Geo<KB>::kOpBytes];                     \
+  __shared__ __attribute__((aligned(1024))) char sA2_[(NST) > 2 ? Geo<KB>::kOpBytes : 16];    \
+  __shared__ __attribute__((aligned(1024))) char sB2_[(NST) > 2 ? Geo<KB>::kOpBytes : 16];    \
+  __shared__ __attribute__((aligned(1024))) char sA3_[(NST) > 3 ? Geo<KB>::kOpBytes : 16];    \
+  __shared__ __attribute__((aligned(1024))) char sB3_[(NST) > 3 ? Geo<KB>::kOpBytes : 16];    \
+  Bufs<NST> B;                                                                                  \
+  {                                                                                             \
+    char* const pa_[4] = {sA0_, sA1_, sA2_, sA3_};                                              \
+    char* const pb_[4] = {sB0_, sB1_, sB2_, sB3_};                                              \
+    _Pragma("unroll") for (int i_ = 0; i_ < (NST); ++i_) {                                      \
+      B.a[i_] = pa_[i_];                                                                        \
+      B.b[i_] = pb_[i_];                                                                        \
+    }                                                                                           \
+  }
+
+// Stages of K for a contraction of length K, padded to a multiple of NST (padding stages
+// load zeros).
+template <typename T, int KB, int NST>
+__host__ __device__ constexpr int padded_stages(int K) {
+  constexpr int KS = KB / (int)sizeof(T);
+  const int n = (K + KS - 1) / KS;
+  return (n + NST - 1) / NST * NST;
+}
+
 // ------------------------------------------------------------------------------------------
 // Forward: per (token tile, vocabulary range) partial log-sum-exp in base 2.
 //   part[split * N + n] = (m, s): m = max_v z*log2(e) over the range, s = sum 2^(z*log2(e) - m)
 // ------------------------------------------------------------------------------------------
-template <typename T>
+template <typename T, int KB, int NST>
 __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E,
                                                          const T* __restrict__ C, int N, int V,
                                                          int D, int n_split, int n_vt,
                                                          int n_items, float2* __restrict__ part) {
-  __shared__ __attribute__((aligned(1024))) char sA0[kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char sB0[kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char sA1[kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char sB1[kOpBytes];
+  CCE_STAGE_BUFFERS(KB, NST, B)
   __shared__ float2 sRed[4][128];
-  constexpr int KS = Traits<T>::kKs;
+  constexpr int KS = KB / (int)sizeof(T);
+  constexpr int I = Geo<KB>::kIssue;
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   if (item >= n_items) return;
   const int tb = item / n_split, sp = item % n_split;
   const int vt0 = (int)((int64_t)sp * n_vt / n_split);
   const int vt1 = (int)((int64_t)(sp + 1) * n_vt / n_split);
-  const int n_k = ((D + 2 * KS - 1) / (2 * KS)) * 2;  // stages per tile, padded to even
+  const int n_k = padded_stages<T, KB, NST>(D);
   const int iters = (vt1 - vt0) * n_k;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
@@ -54,54 +81,82 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
   zero_acc(acc);
 
   const int64_t ldb = (int64_t)D * sizeof(T);
-  uint32_t off[8];  // C and E tiles share the row length, hence the offsets
-  kmajor_offsets(off, ldb, wave, lane);
-  auto issue = [&](int it, char* a, char* b) {
+  uint32_t off[I];  // C and E tiles share the row length, hence the offsets
+  kmajor_offsets<KB>(off, ldb, wave, lane);
+  auto issue = [&](int it) {
     const int vt = vt0 + it / n_k, k0 = (it % n_k) * KS;
-    const int kc = (D - k0) / Traits<T>::kEpc;  // <= 0 on the padding stage: all zeros
+    const int kc = (D - k0) / Traits<T>::kEpc;  // <= 0 on padding stages: all zeros
     const int64_t kb = (int64_t)k0 * sizeof(T);
-    kmajor_issue(C + (int64_t)vt * kTile * D + k0, off, tile_records(V, (int64_t)vt * kTile, ldb, kb),
-                 kc, a, wave, lane);
-    kmajor_issue(E + (int64_t)tok0 * D + k0, off, tile_records(N, tok0, ldb, kb), kc, b, wave,
-                 lane);
+    const T* oa = C + (int64_t)vt * kTile * D + k0;
+    const T* ob = E + (int64_t)tok0 * D + k0;
+    const int ra = tile_records(V, (int64_t)vt * kTile, ldb, kb);
+    const int rb = tile_records(N, tok0, ldb, kb);
+    return [=, &off](char* a, char* b, int p) {
+      const int q0 = p * Slices<KB>::kPer, q1 = q0 + Slices<KB>::kPer;
+      kmajor_issue<KB>(oa, off, ra, kc, a, wave, lane, q0, q1);
+      kmajor_issue<KB>(ob, off, rb, kc, b, wave, lane, q0, q1);
+    };
   };
-  // Online log-sum-exp update for the finished tile, one token column group (ni) at a time so
-  // that only 64 accumulators are in flight; each group is cleared for the next tile.
+  // Online log-sum-exp update for the finished tile, one token column group (ni) at a time.
+  // Single pass against the running maximum m: t = z log2(e) - m, s += sum 2^t, with eight
+  // independent partial sums and maxima so the VALU work pipelines; afterwards the pair is
+  // rebased to the new maximum.  If some value exceeds the running maximum by more than 2^64
+  // (always on the first tile, where m = -inf), the wave recomputes the group exactly.
   auto epilogue = [&](int vt) {
     const int vbase = vt * kTile + 128 * wm;
     const bool full = vt * kTile + kTile <= V;
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
-      float mx = -INFINITY;
+      float x[64];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const bool ok = full || vbase + 32 * mi + acc_row(r, lane) < V;
-          mx = fmaxf(mx, ok ? acc[mi][ni][r] : -INFINITY);
-        }
-      const float m_new = fmaxf(m_run[ni], mx * kLog2e);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      float s = s_run[ni] * exp2_fast(m_run[ni] - m_use);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool ok = full || vbase + 32 * mi + acc_row(r, lane) < V;
-          const float e = exp2_fast(__builtin_fmaf(acc[mi][ni][r], kLog2e, -m_use));
-          s += ok ? e : 0.f;
+          const float z = acc[mi][ni][r];
+          x[16 * mi + r] = (full || vbase + 32 * mi + acc_row(r, lane) < V) ? z : -INFINITY;
           acc[mi][ni][r] = 0.f;
         }
-      s_run[ni] = s;
-      m_run[ni] = m_new;
+      const float m = m_run[ni];
+      float ps[8], pm[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) { ps[k] = 0.f; pm[k] = -INFINITY; }
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        const float t = __builtin_fmaf(x[i], kLog2e, -m);
+        ps[i & 7] += exp2_fast(t);
+        pm[i & 7] = fmaxf(pm[i & 7], t);
+      }
+      const float tmax = fmaxf(fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3])),
+                               fmaxf(fmaxf(pm[4], pm[5]), fmaxf(pm[6], pm[7])));
+      // exact path also while m = -inf (nothing seen yet: t would be -inf + inf for masked rows)
+      if (__ballot(!(tmax <= 64.f) || m == -INFINITY) != 0ull) {
+        // exact update (rare): new maximum first, then the sum against it
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) mx = fmaxf(mx, x[i]);
+        const float m_new = fmaxf(m, mx * kLog2e);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ps[k] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) ps[i & 7] += exp2_fast(__builtin_fmaf(x[i], kLog2e, -m_use));
+        const float tile = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+        s_run[ni] = s_run[ni] * exp2_fast(m - m_use) + tile;
+        m_run[ni] = m_new;
+      } else {
+        const float tile = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+        const float up = fmaxf(tmax, 0.f);       // rebase so that s stays O(number of terms)
+        s_run[ni] = (s_run[ni] + tile) * exp2_fast(-up);
+        m_run[ni] = m + up;
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   const int n_tiles = vt1 - vt0;
-  if (iters > 0) issue(0, sA0, sB0);
+  run_prologue<KB, NST>(iters, issue, B);
   for (int t = 0; t < n_tiles; ++t) {
-    run_stream<T, true, true>(t * n_k, n_k, iters, issue, sA0, sB0, sA1, sB1, acc, wm, wn, lane);
+    run_stream<T, KB, NST, true, true>(t * n_k, n_k, iters, issue, B, acc, wm, wn, lane);
     epilogue(vt0 + t);
   }
 
@@ -194,83 +249,139 @@ __global__ __launch_bounds__(kThreads) void k_fwd_finish(
 // and store G (chunk-local columns, row stride ldg) for the blocks that are kept.
 //   flags[(n / 64) * fstride + v_local / 64] = 1 if the block is skipped (G not stored).
 // ------------------------------------------------------------------------------------------
+// Arguments of the backward steps for one vocabulary chunk [v0, v0 + vc).
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void k_bwd_g(
-    const T* __restrict__ E, const T* __restrict__ C, const int64_t* __restrict__ tgt,
-    const float* __restrict__ lse, const float* __restrict__ dloss, int64_t dstride, int N,
-    int V, int D, int v0, int vc, int n_tb, int n_vtc, T* __restrict__ G, int64_t ldg,
-    uint8_t* __restrict__ flags, int fstride, float eps, int64_t ignore_index,
-    unsigned long long* __restrict__ skip_count) {
-  __shared__ __attribute__((aligned(1024))) char sA0[kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char sB0[kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char sA1[kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char sB1[kOpBytes];
-  constexpr int KS = Traits<T>::kKs;
+struct BwdArgs {
+  const T* E;                 // [N, D]
+  const T* C;                 // [V, D]
+  const int64_t* tgt;         // [N]
+  const float* lse;           // [N]
+  const float* dloss;         // [N] or scalar (dstride 0)
+  int64_t dstride;
+  int N, V, D, n_pad;         // n_pad: N rounded up to the tile
+  int v0, vc;                 // chunk origin and width
+  int n_tb, n_vtc, n_dt;      // token tiles, chunk vocabulary tiles, hidden-dimension tiles
+  T* G;                       // [n_pad, ldg] softmax-gradient store of the chunk
+  int64_t ldg;
+  uint8_t* flags;             // [n_pad / 64, fstride] skipped 64 x 64 blocks of the chunk
+  int fstride;
+  float eps;
+  int64_t ignore_index;
+  unsigned long long* skip_count;
+  float* dE;                  // [N, D]
+  float* dC;                  // [V, D]
+  int accumulate;             // dE += (later chunks) instead of dE = (first chunk)
+};
 
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+template <typename T, int KB, int NST>
+__device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const Bufs<NST>& B) {
+  const T* __restrict__ E = A.E;
+  const T* __restrict__ C = A.C;
+  const int64_t* __restrict__ tgt = A.tgt;
+  const float* __restrict__ lse = A.lse;
+  const float* __restrict__ dloss = A.dloss;
+  const int64_t dstride = A.dstride;
+  const int N = A.N, D = A.D, v0 = A.v0, vc = A.vc, n_tb = A.n_tb, n_vtc = A.n_vtc;
+  T* __restrict__ G = A.G;
+  const int64_t ldg = A.ldg;
+  uint8_t* __restrict__ flags = A.flags;
+  const int fstride = A.fstride;
+  const float eps = A.eps;
+  const int64_t ignore_index = A.ignore_index;
+  unsigned long long* __restrict__ skip_count = A.skip_count;
+  constexpr int KS = KB / (int)sizeof(T);
+  constexpr int I = Geo<KB>::kIssue;
+
   int tb, vt;
   grouped_tile(lin, n_vtc, tb, vt);
   if (tb >= n_tb || vt >= n_vtc) return;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   const int tok0 = tb * kTile, vl0 = vt * kTile;  // vl0: chunk-local first vocab row
-  const int n_k = ((D + 2 * KS - 1) / (2 * KS)) * 2;  // padded to even: last stage may be zeros
+  const int n_k = padded_stages<T, KB, NST>(D);
   const T* Cc = C + (int64_t)v0 * D;
 
   f32x16_t acc[4][4];
   zero_acc(acc);
   const int64_t ldb = (int64_t)D * sizeof(T);
-  uint32_t off[8];
-  kmajor_offsets(off, ldb, wave, lane);
-  auto issue = [&](int it, char* a, char* b) {
+  uint32_t off[I];
+  kmajor_offsets<KB>(off, ldb, wave, lane);
+  auto issue = [&](int it) {
     const int k0 = it * KS;
     const int kc = (D - k0) / Traits<T>::kEpc;
     const int64_t kb = (int64_t)k0 * sizeof(T);
-    kmajor_issue(Cc + (int64_t)vl0 * D + k0, off, tile_records(vc, vl0, ldb, kb), kc, a, wave,
-                 lane);
-    kmajor_issue(E + (int64_t)tok0 * D + k0, off, tile_records(N, tok0, ldb, kb), kc, b, wave,
-                 lane);
+    const T* oa = Cc + (int64_t)vl0 * D + k0;
+    const T* ob = E + (int64_t)tok0 * D + k0;
+    const int ra = tile_records(vc, vl0, ldb, kb);
+    const int rb = tile_records(N, tok0, ldb, kb);
+    return [=, &off](char* a, char* b, int p) {
+      const int q0 = p * Slices<KB>::kPer, q1 = q0 + Slices<KB>::kPer;
+      kmajor_issue<KB>(oa, off, ra, kc, a, wave, lane, q0, q1);
+      kmajor_issue<KB>(ob, off, rb, kc, b, wave, lane, q0, q1);
+    };
   };
-  issue(0, sA0, sB0);
-  run_stream<T, true, true>(0, n_k, n_k, issue, sA0, sB0, sA1, sB1, acc, wm, wn, lane);
-
-  // epilogue: per column (token) constants
-  const bool filter = eps > 0.f;
-  bool sig[2][2] = {{false, false}, {false, false}};
+  // per column (token) constants, loaded before the main loop so their latency is hidden
   float coef[4], lse2[4];
   int trow[4];
+  bool valid[4];
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
     const int n = tok0 + 128 * wn + 32 * ni + (lane & 31);
-    bool valid = false;
+    bool ok = false;
     float w = 0.f, l2 = 0.f;
     int tr = -1;
     if (n < N) {
       const int64_t t = tgt[n];
-      valid = t != ignore_index;
+      ok = t != ignore_index;
       w = dloss[(int64_t)n * dstride];
       l2 = lse[n] * kLog2e;
       const int64_t tl = t - (int64_t)v0 - vl0 - 128 * wm;  // target row within this wave's rows
-      tr = (valid && tl >= 0 && tl < 128) ? (int)tl : -1;
+      tr = (ok && tl >= 0 && tl < 128) ? (int)tl : -1;
     }
-    coef[ni] = valid ? w : 0.f;
+    valid[ni] = ok;
+    coef[ni] = ok ? w : 0.f;
     lse2[ni] = l2;
-    trow[ni] = valid ? tr : -2;  // -2 marks an ignored or padded column
+    trow[ni] = tr;
   }
+
+  run_prologue<KB, NST>(n_k, issue, B);
+  run_stream<T, KB, NST, true, true>(0, n_k, n_k, issue, B, acc, wm, wn, lane);
+
+  // epilogue: p = 2^(z log2 e - lse log2 e); G = coef (p - [row == target]); per lane and
+  // 64 x 64 block the largest p (independent maxima, no serial chains)
+  const bool filter = eps > 0.f;
   const bool full = vl0 + kTile <= vc;
+  float pmax[2][4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < 4; ++ni) pmax[a][ni] = 0.f;
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * mi + acc_row(r, lane);  // row within this wave's 128 rows
-        float p = exp2_fast(acc[mi][ni][r] * kLog2e - lse2[ni]);
+        float p = exp2_fast(__builtin_fmaf(acc[mi][ni][r], kLog2e, -lse2[ni]));
         if (!full && vl0 + 128 * wm + row >= vc) p = 0.f;
-        const bool is_t = row == trow[ni];
-        sig[mi >> 1][ni >> 1] |= (trow[ni] != -2) && (p >= eps || is_t);
-        acc[mi][ni][r] = coef[ni] * (is_t ? p - 1.f : p);
+        pmax[mi >> 1][ni] = fmaxf(pmax[mi >> 1][ni], p);
+        acc[mi][ni][r] = __builtin_fmaf(coef[ni], p, row == trow[ni] ? -coef[ni] : 0.f);
       }
+  bool sig[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      bool any = false;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ni = 2 * b + h;
+        const bool has_t = trow[ni] >= 64 * a && trow[ni] < 64 * a + 64;
+        any |= valid[ni] && (pmax[a][ni] >= eps || has_t);
+      }
+      sig[a][b] = any;
+    }
 
   // block decisions (wave-wide), flags, statistics
   int n_skipped = 0;
@@ -365,7 +476,7 @@ __device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, 
 // skipped within the stage (its operand chunk is loaded as zeros).
 //   rowwise: flags of stage s are flags[(fr0 + b) * fstride + s * KS / 64]   (dE: K = vocab)
 //   else   : flags of stage s are flags[(s * KS / 64) * fstride + fc0 + b]   (dC: K = tokens)
-template <int KS>
+template <int KS, int NST>
 __device__ __forceinline__ int build_stage_list(const uint8_t* __restrict__ flags, int fstride,
                                                 int n_stages, bool rowwise, int fixed0,
                                                 int* list, int* wave_cnt) {
@@ -395,34 +506,34 @@ __device__ __forceinline__ int build_stage_list(const uint8_t* __restrict__ flag
     total += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
     __syncthreads();
   }
-  // pad to an even count with an all-zero stage (every block masked), so the main loop runs
-  // whole pairs of stages
-  if (total & 1) {
-    if (threadIdx.x == 0) list[total] = 15;
+  // pad to a multiple of NST with all-zero stages (every block masked), so the pipeline runs
+  // whole rounds of stages
+  const int padded = (total + NST - 1) / NST * NST;
+  if (padded != total) {
+    if ((int)threadIdx.x < padded - total) list[total + threadIdx.x] = 15;
     __syncthreads();
-    ++total;
   }
-  return total;
+  return padded;
 }
 
 // ------------------------------------------------------------------------------------------
 // Backward, step 2: dE[tok tile, d tile] (+)= sum over the chunk's vocabulary of
 // G[tok, v] C[v0 + v, d].  A = G (K-major, K = vocab), B = C chunk (MN-major).
 // ------------------------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void k_bwd_de(
-    const T* __restrict__ G, int64_t ldg, const T* __restrict__ Cc, int D, int N, int kv,
-    int vc, const uint8_t* __restrict__ flags, int fstride, int n_tb, int n_dt,
-    float* __restrict__ dE, int accumulate) {
-  __shared__ __attribute__((aligned(1024))) char sA0[kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char sB0[kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char sA1[kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char sB1[kOpBytes];
-  __shared__ int sList[8192 / 32 + 8];  // stages of one chunk (+1 padding)
-  __shared__ int sCnt[4];
-  constexpr int KS = Traits<T>::kKs;
-
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+template <typename T, int KB, int NST>
+__device__ __forceinline__ void tile_bwd_de(const BwdArgs<T>& A, int lin, const Bufs<NST>& B,
+                                            int* sList, int* sCnt) {
+  constexpr int KS = KB / (int)sizeof(T);
+  constexpr int I = Geo<KB>::kIssue;
+  const T* __restrict__ G = A.G;
+  const int64_t ldg = A.ldg;
+  const T* __restrict__ Cc = A.C + (int64_t)A.v0 * A.D;
+  const int D = A.D, N = A.N, vc = A.vc, n_tb = A.n_tb, n_dt = A.n_dt;
+  const int kv = (vc + KS - 1) / KS * KS;
+  const uint8_t* __restrict__ flags = A.flags;
+  const int fstride = A.fstride;
+  float* __restrict__ dE = A.dE;
+  const int accumulate = A.accumulate;
   int tb, dt;
   grouped_tile(lin, n_dt, tb, dt);
   if (tb >= n_tb || dt >= n_dt) return;
@@ -430,26 +541,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_de(
   const int wm = wave >> 1, wn = wave & 1;
   const int tok0 = tb * kTile, d0 = dt * kTile;
   const int n_stages = kv / KS;
-  const int n_act = build_stage_list<KS>(flags, fstride, n_stages, true, tb * 4, sList, sCnt);
+  const int n_act =
+      build_stage_list<KS, NST>(flags, fstride, n_stages, true, tb * 4, sList, sCnt);
 
   f32x16_t acc[4][4];
   zero_acc(acc);
   if (n_act == 0 && accumulate) return;
   const int64_t ldb = (int64_t)D * sizeof(T);
-  uint32_t offA[8], offB[8];
-  kmajor_offsets(offA, ldg * (int64_t)sizeof(T), wave, lane);
-  mn_offsets<T>(offB, ldb, d0, D, wave, lane);
-  auto issue = [&](int i, char* a, char* b) {
+  uint32_t offA[I], offB[I];
+  kmajor_offsets<KB>(offA, ldg * (int64_t)sizeof(T), wave, lane);
+  mn_offsets<T, KB>(offB, ldb, d0, D, wave, lane);
+  auto issue = [&](int i) {
     const int e = __builtin_amdgcn_readfirstlane(sList[i]);
     const int k0 = (e >> 4) * KS;
     const bool zero = (e >> wave) & 1;  // wave w loads the tile's token rows 64 w .. 64 w + 63
-    kmajor_issue(G + (int64_t)tok0 * ldg + k0, offA, zero ? 0 : kRecords, 8, a, wave, lane);
-    mn_issue<T>(Cc + (int64_t)k0 * D + d0, offB, tile_records(vc, k0, ldb, (int64_t)d0 * sizeof(T)),
-                0u, b, wave, lane);
+    const T* oa = G + (int64_t)tok0 * ldg + k0;
+    const T* ob = Cc + (int64_t)k0 * D + d0;
+    const int ra = zero ? 0 : kRecords;
+    const int rb = tile_records(vc, k0, ldb, (int64_t)d0 * sizeof(T));
+    return [=, &offA, &offB](char* a, char* b, int p) {
+      const int q0 = p * Slices<KB>::kPer, q1 = q0 + Slices<KB>::kPer;
+      kmajor_issue<KB>(oa, offA, ra, Geo<KB>::kChunks, a, wave, lane, q0, q1);
+      mn_issue<T, KB>(ob, offB, rb, 0u, b, wave, lane, q0, q1);
+    };
   };
   if (n_act > 0) {
-    issue(0, sA0, sB0);
-    run_stream<T, true, false>(0, n_act, n_act, issue, sA0, sB0, sA1, sB1, acc, wm, wn, lane);
+    run_prologue<KB, NST>(n_act, issue, B);
+    run_stream<T, KB, NST, true, false>(0, n_act, n_act, issue, B, acc, wm, wn, lane);
   }
   store_tile(dE, D, tok0 + 128 * wm, N, d0 + 128 * wn, D, acc, lane, accumulate != 0);
 }
@@ -458,20 +576,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_de(
 // Backward, step 3: dC[v0 + v, d] = sum over tokens of G[tok, v] E[tok, d] for the chunk.
 // A = G (MN-major, K = tokens), B = E (MN-major).
 // ------------------------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void k_bwd_dc(
-    const T* __restrict__ G, int64_t ldg, const T* __restrict__ E, int D, int N, int n_pad,
-    int vc, const uint8_t* __restrict__ flags, int fstride, int n_vtc, int n_dt,
-    float* __restrict__ dCc) {
-  __shared__ __attribute__((aligned(1024))) char sA0[kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char sB0[kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char sA1[kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char sB1[kOpBytes];
-  __shared__ int sList[4096 + 8];
-  __shared__ int sCnt[4];
-  constexpr int KS = Traits<T>::kKs;
+constexpr int kDcPiece = 4096;   // token stages handled per stage list of the dC product
 
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+template <typename T, int KB, int NST>
+__device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const Bufs<NST>& B,
+                                            int* sList, int* sCnt) {
+  constexpr int KS = KB / (int)sizeof(T);
+  constexpr int I = Geo<KB>::kIssue;
+  constexpr int kPiece = kDcPiece;
+  const T* __restrict__ G = A.G;
+  const int64_t ldg = A.ldg;
+  const T* __restrict__ E = A.E;
+  const int D = A.D, N = A.N, n_pad = A.n_pad, vc = A.vc, n_vtc = A.n_vtc, n_dt = A.n_dt;
+  const uint8_t* __restrict__ flags = A.flags;
+  const int fstride = A.fstride;
+  float* __restrict__ dCc = A.dC + (int64_t)A.v0 * A.D;
   int vt, dt;
   grouped_tile(lin, n_dt, vt, dt);
   if (vt >= n_vtc || dt >= n_dt) return;
@@ -479,32 +598,70 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dc(
   const int wm = wave >> 1, wn = wave & 1;
   const int vl0 = vt * kTile, d0 = dt * kTile;
   const int n_stages = n_pad / KS;
-
   const int64_t ldb = (int64_t)D * sizeof(T);
-  uint32_t offA[8], offB[8];
-  mn_offsets<T>(offA, ldg * (int64_t)sizeof(T), vl0, (int)ldg, wave, lane);
-  mn_offsets<T>(offB, ldb, d0, D, wave, lane);
+  uint32_t offA[I], offB[I];
+  mn_offsets<T, KB>(offA, ldg * (int64_t)sizeof(T), vl0, (int)ldg, wave, lane);
+  mn_offsets<T, KB>(offB, ldb, d0, D, wave, lane);
   f32x16_t acc[4][4];
   zero_acc(acc);
-  // token stages are processed in pieces of at most 4096 list entries
-  for (int sbase = 0; sbase < n_stages; sbase += 4096) {
-    const int cnt = min(4096, n_stages - sbase);
-    const int n_act = build_stage_list<KS>(flags + (int64_t)((sbase * KS) >> 6) * fstride,
-                                           fstride, cnt, false, vt * 4, sList, sCnt);
-    auto issue = [&](int i, char* a, char* b) {
+  for (int sbase = 0; sbase < n_stages; sbase += kPiece) {
+    const int cnt = min(kPiece, n_stages - sbase);
+    const int n_act = build_stage_list<KS, NST>(flags + (int64_t)((sbase * KS) >> 6) * fstride,
+                                                fstride, cnt, false, vt * 4, sList, sCnt);
+    auto issue = [&](int i) {
       const int e = __builtin_amdgcn_readfirstlane(sList[i]);
       const int k0 = (sbase + (e >> 4)) * KS;
-      mn_issue<T>(G + (int64_t)k0 * ldg + vl0, offA, kRecords, (uint32_t)(e & 15), a, wave, lane);
-      mn_issue<T>(E + (int64_t)k0 * D + d0, offB, tile_records(N, k0, ldb, (int64_t)d0 * sizeof(T)),
-                  0u, b, wave, lane);
+      const T* oa = G + (int64_t)k0 * ldg + vl0;
+      const T* ob = E + (int64_t)k0 * D + d0;
+      const uint32_t zc = (uint32_t)(e & 15);
+      const int rb = tile_records(N, k0, ldb, (int64_t)d0 * sizeof(T));
+      return [=, &offA, &offB](char* a, char* b, int p) {
+        const int q0 = p * Slices<KB>::kPer, q1 = q0 + Slices<KB>::kPer;
+        mn_issue<T, KB>(oa, offA, kRecords, zc, a, wave, lane, q0, q1);
+        mn_issue<T, KB>(ob, offB, rb, 0u, b, wave, lane, q0, q1);
+      };
     };
     if (n_act > 0) {
-      issue(0, sA0, sB0);
-      run_stream<T, false, false>(0, n_act, n_act, issue, sA0, sB0, sA1, sB1, acc, wm, wn, lane);
+      run_prologue<KB, NST>(n_act, issue, B);
+      run_stream<T, KB, NST, false, false>(0, n_act, n_act, issue, B, acc, wm, wn, lane);
     }
     __syncthreads();
   }
   store_tile(dCc, D, vl0 + 128 * wm, vc, d0 + 128 * wn, D, acc, lane, false);
+}
+
+// Work items of the backward launches, in super-blocks of 4 x 8 tiles.
+__host__ __device__ inline int bwd_items(int rows, int cols) {
+  return ((rows + 3) / 4) * ((cols + 7) / 8) * 32;
+}
+
+// Backward step 1 alone (the first chunk): one G tile per workgroup.
+template <typename T, int KB, int NST>
+__global__ __launch_bounds__(kThreads, 1) void k_bwd_g(BwdArgs<T> A) {
+  CCE_STAGE_BUFFERS(KB, NST, B)
+  tile_bwd_g<T, KB, NST>(A, xcd_remap(blockIdx.x, gridDim.x), B);
+}
+
+// Backward steps 2 and 3 of chunk c (dE and dC tiles, the long ones) fused with step 1 of
+// chunk c + 1 (G tiles of the next chunk into the other G buffer, the short ones), so the
+// short tiles fill the CUs that the 2 x (N/256) x (D/256) long tiles leave idle.  Workgroups
+// [0, r_de) compute dE tiles, [r_de, r_de + r_dc) dC tiles, the rest G tiles of `next`
+// (none when n_next_items == 0).  Each range is a multiple of 8 and renumbered per XCD.
+template <typename T, int KB, int NST>
+__global__ __launch_bounds__(kThreads, 1) void k_bwd_fused(BwdArgs<T> A, BwdArgs<T> next,
+                                                           int r_de, int r_dc) {
+  CCE_STAGE_BUFFERS(KB, NST, B)
+  __shared__ int sList[kDcPiece + NST];
+  __shared__ int sCnt[4];
+  const int b = blockIdx.x;
+  if (b < r_de) {
+    tile_bwd_de<T, KB, NST>(A, xcd_remap(b, r_de), B, sList, sCnt);
+  } else if (b < r_de + r_dc) {
+    tile_bwd_dc<T, KB, NST>(A, xcd_remap(b - r_de, r_dc), B, sList, sCnt);
+  } else {
+    const int n = (int)gridDim.x - r_de - r_dc;
+    tile_bwd_g<T, KB, NST>(next, xcd_remap(b - r_de - r_dc, n), B);
+  }
 }
 
 // p[0..n) = 0 (a kernel rather than a memset, so the call stays safe under graph capture)

@@ -32,7 +32,6 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kThreads = 256;
 constexpr int kTile = 256;           // tile rows (M) and columns (N)
-constexpr int kOpBytes = 32768;      // one operand's share of one stage
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -78,22 +77,42 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* lds, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
 }
 
-// K-major operand: 256 rows x 128 bytes per stage.  LDS slot (row r, chunk pc) holds logical
-// K chunk pc ^ ((r >> 1) & 7).  Instruction q of wave w fills rows 8 (8 w + q) .. + 7, so the
-// 8 instructions of wave w cover tile rows 64 w .. 64 w + 63.
-__device__ __forceinline__ int kmajor_row(int wave, int q, int lane) {
-  return (wave * 8 + q) * 8 + (lane >> 3);
-}
-__device__ __forceinline__ int kmajor_chunk(int r, int lane) { return (lane & 7) ^ ((r >> 1) & 7); }
+// Stage geometry.  KB = bytes of K per K-major operand row per stage (128 or 64), so one
+// operand's share of a stage is 256 x KB bytes, and each wave issues KB / 16 direct-to-LDS
+// instructions per operand and stage.
+template <int KB>
+struct Geo {
+  static_assert(KB == 128 || KB == 64, "stage K bytes");
+  static constexpr int kChunks = KB / 16;         // 16-byte chunks per K-major row
+  static constexpr int kIssue = KB / 16;          // instructions per wave per operand
+  static constexpr int kRowsPerWin = 256 / KB;    // K-major rows per 256-byte bank window
+  static constexpr int kOpBytes = 256 * KB;       // one operand's share of one stage
+  static constexpr int kGroups = KB / 32;         // MFMA k-groups per stage
+};
 
-// Offsets of this lane's 8 chunks relative to the tile origin (row0, k0).  Rows past the
+// K-major operand: 256 rows x KB bytes per stage.  LDS slot (row r, chunk pc) holds logical K
+// chunk pc ^ f(r), f(r) = (r / rows-per-window) mod chunks, which spreads the 16 rows read by
+// one quarter-wave over distinct banks.  Instruction q of wave w fills 1 KB of consecutive
+// LDS, i.e. rows (w * I + q) * (1024 / KB) onwards (I = instructions per wave), so wave w
+// covers rows 64 w .. 64 w + 63.
+template <int KB>
+__device__ __forceinline__ int kmajor_row(int wave, int q, int lane) {
+  return (wave * Geo<KB>::kIssue + q) * (1024 / KB) + lane / Geo<KB>::kChunks;
+}
+template <int KB>
+__device__ __forceinline__ int kmajor_chunk(int r, int lane) {
+  return (lane % Geo<KB>::kChunks) ^ ((r / Geo<KB>::kRowsPerWin) % Geo<KB>::kChunks);
+}
+
+// Offsets of this lane's chunks relative to the tile origin (row0, k0).  Rows past the
 // operand's end are cut off by the descriptor range (tile_records), not here.
-__device__ __forceinline__ void kmajor_offsets(uint32_t (&off)[8], int64_t ld_bytes, int wave,
-                                               int lane) {
+template <int KB>
+__device__ __forceinline__ void kmajor_offsets(uint32_t (&off)[Geo<KB>::kIssue], int64_t ld_bytes,
+                                               int wave, int lane) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int r = kmajor_row(wave, q, lane);
-    off[q] = (uint32_t)(r * ld_bytes) + 16u * kmajor_chunk(r, lane);
+  for (int q = 0; q < Geo<KB>::kIssue; ++q) {
+    const int r = kmajor_row<KB>(wave, q, lane);
+    off[q] = (uint32_t)(r * ld_bytes) + 16u * kmajor_chunk<KB>(r, lane);
   }
 }
 
@@ -105,57 +124,64 @@ __device__ __forceinline__ int tile_records(int64_t row_lim, int64_t row0, int64
   return b <= 0 ? 0 : (b > kRecords ? kRecords : (int)b);
 }
 
-// One stage.  k_chunks = valid 16-byte K chunks left from k0 (>= 8: full stage).
-__device__ __forceinline__ void kmajor_issue(const void* origin, const uint32_t (&off)[8],
-                                             int records, int k_chunks, char* lds, int wave,
-                                             int lane) {
+// One slice of a stage: instructions [Q0, Q1) of this wave.  k_chunks = valid 16-byte K
+// chunks left from k0 (>= chunks per row: full stage).
+template <int KB>
+__device__ __forceinline__ void kmajor_issue(const void* origin,
+                                             const uint32_t (&off)[Geo<KB>::kIssue], int records,
+                                             int k_chunks, char* lds, int wave, int lane,
+                                             int q0 = 0, int q1 = Geo<KB>::kIssue) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(origin, records);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int q = 0; q < Geo<KB>::kIssue; ++q) {
+    if (q < q0 || q >= q1) continue;
     uint32_t o = off[q];
-    if (k_chunks < 8) o = kmajor_chunk(kmajor_row(wave, q, lane), lane) < k_chunks ? o : kOob;
-    lds_load16(rs, lds + (wave * 8 + q) * 1024, o);
+    if (k_chunks < Geo<KB>::kChunks)
+      o = kmajor_chunk<KB>(kmajor_row<KB>(wave, q, lane), lane) < k_chunks ? o : kOob;
+    lds_load16(rs, lds + (wave * Geo<KB>::kIssue + q) * 1024, o);
   }
 }
 
-// MN-major operand: (32768 / RB) rows of k, RB = 256 * sizeof(T) bytes of columns per row.
+// MN-major operand: KB / sizeof(T) rows of k, each RB = 256 * sizeof(T) bytes of columns.
 // LDS slot (row k, chunk pc) holds logical column chunk pc ^ (4 * (k & 3)).
-template <typename T>
+template <typename T, int KB>
 __device__ __forceinline__ int mn_row(int wave, int q, int lane) {
   constexpr int RB = 256 * (int)sizeof(T);
-  return ((wave * 8 + q) * 1024 + lane * 16) / RB;
+  return ((wave * Geo<KB>::kIssue + q) * 1024 + lane * 16) / RB;
 }
-template <typename T>
+template <typename T, int KB>
 __device__ __forceinline__ int mn_col(int wave, int q, int lane) {  // first column of the chunk
   constexpr int RB = 256 * (int)sizeof(T);
-  const int r = mn_row<T>(wave, q, lane);
-  const int pc = (((wave * 8 + q) * 1024 + lane * 16) % RB) >> 4;
+  const int r = mn_row<T, KB>(wave, q, lane);
+  const int pc = (((wave * Geo<KB>::kIssue + q) * 1024 + lane * 16) % RB) >> 4;
   return (pc ^ (4 * (r & 3))) * Traits<T>::kEpc;
 }
 
 // Offsets for a tile whose first column is col0 (columns >= col_lim masked here; rows past
 // the end are cut off by the descriptor range).
-template <typename T>
-__device__ __forceinline__ void mn_offsets(uint32_t (&off)[8], int64_t ld_bytes, int col0,
-                                           int col_lim, int wave, int lane) {
+template <typename T, int KB>
+__device__ __forceinline__ void mn_offsets(uint32_t (&off)[Geo<KB>::kIssue], int64_t ld_bytes,
+                                           int col0, int col_lim, int wave, int lane) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int r = mn_row<T>(wave, q, lane), c = mn_col<T>(wave, q, lane);
+  for (int q = 0; q < Geo<KB>::kIssue; ++q) {
+    const int r = mn_row<T, KB>(wave, q, lane), c = mn_col<T, KB>(wave, q, lane);
     off[q] = (col0 + c < col_lim) ? (uint32_t)(r * ld_bytes) + (uint32_t)(c * sizeof(T)) : kOob;
   }
 }
 
-// One stage.  zero_cols bit b = load zeros for columns 64 b .. 64 b + 63 of the tile.
-template <typename T>
-__device__ __forceinline__ void mn_issue(const void* origin, const uint32_t (&off)[8],
+// One slice of a stage: instructions [Q0, Q1).  zero_cols bit b = load zeros for columns
+// 64 b .. 64 b + 63 of the tile.
+template <typename T, int KB>
+__device__ __forceinline__ void mn_issue(const void* origin, const uint32_t (&off)[Geo<KB>::kIssue],
                                          int records, uint32_t zero_cols, char* lds, int wave,
-                                         int lane) {
+                                         int lane, int q0 = 0, int q1 = Geo<KB>::kIssue) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(origin, records);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int q = 0; q < Geo<KB>::kIssue; ++q) {
+    if (q < q0 || q >= q1) continue;
     uint32_t o = off[q];
-    if (zero_cols) o = ((zero_cols >> (mn_col<T>(wave, q, lane) >> 6)) & 1u) ? kOob : o;
-    lds_load16(rs, lds + (wave * 8 + q) * 1024, o);
+    if (zero_cols) o = ((zero_cols >> (mn_col<T, KB>(wave, q, lane) >> 6)) & 1u) ? kOob : o;
+    lds_load16(rs, lds + (wave * Geo<KB>::kIssue + q) * 1024, o);
   }
 }
 
@@ -165,12 +191,12 @@ __device__ __forceinline__ void mn_issue(const void* origin, const uint32_t (&of
 // ---------------------------------------------------------------------------------------
 
 // K-major: row is the tile row of this lane.
-template <typename T>
+template <typename T, int KB>
 __device__ __forceinline__ typename Traits<T>::frag_t frag_k(const char* tile, int row, int g,
                                                              int lane) {
   const int lc = 2 * g + (lane >> 5);
-  const int pc = lc ^ ((row >> 1) & 7);
-  return *(const typename Traits<T>::frag_t*)(tile + row * 128 + pc * 16);
+  const int pc = lc ^ ((row / Geo<KB>::kRowsPerWin) % Geo<KB>::kChunks);
+  return *(const typename Traits<T>::frag_t*)(tile + row * KB + pc * 16);
 }
 
 // MN-major bf16: two transposing reads of 4 x 16 bits.  Within each 16-lane group the
@@ -201,11 +227,11 @@ __device__ __forceinline__ f32x4_t frag_mn_f32(const char* tile, int col0, int g
   return v;
 }
 
-template <typename T, bool KMAJOR>
+template <typename T, int KB, bool KMAJOR>
 __device__ __forceinline__ typename Traits<T>::frag_t frag(const char* tile, int blk0, int g,
                                                            int lane) {
   if constexpr (KMAJOR) {
-    return frag_k<T>(tile, blk0 + (lane & 31), g, lane);
+    return frag_k<T, KB>(tile, blk0 + (lane & 31), g, lane);
   } else if constexpr (sizeof(T) == 2) {
     return frag_mn_bf16(tile, blk0, g, lane);
   } else {
@@ -221,73 +247,130 @@ __device__ __forceinline__ void mma(f32x16_t& acc, const f32x4_t& a, const f32x4
   for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], acc, 0, 0, 0);
 }
 
-// One stage of MFMAs for this wave: 4 k-groups x 4 x 4 blocks.
-template <typename T, bool AK, bool BK>
+// One stage of MFMAs for this wave: KB / 32 k-groups x 4 x 4 blocks.  Before the MFMAs of
+// k-group g it reads the fragments of group g + 1 from LDS and calls part(g), which issues
+// slice g of a later stage's direct-to-LDS loads; spreading the loads over the stage keeps
+// the address units from stalling the MFMA issue.  The scheduling barriers keep the compiler
+// from regrouping the reads, loads and MFMAs.
+struct NoIssue {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <typename T, int KB, bool AK, bool BK, typename Part = NoIssue>
 __device__ __forceinline__ void compute_stage(const char* As, const char* Bs,
-                                              f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
+                                              f32x16_t (&acc)[4][4], int wm, int wn, int lane,
+                                              Part&& part = Part()) {
   typedef typename Traits<T>::frag_t F;
+  F a[2][4], b[2][4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    F a[4], b[4];
+  for (int i = 0; i < 4; ++i) a[0][i] = frag<T, KB, AK>(As, 128 * wm + 32 * i, 0, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = frag<T, AK>(As, 128 * wm + 32 * i, g, lane);
+  for (int i = 0; i < 4; ++i) b[0][i] = frag<T, KB, BK>(Bs, 128 * wn + 32 * i, 0, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = frag<T, BK>(Bs, 128 * wn + 32 * i, g, lane);
+  for (int g = 0; g < Geo<KB>::kGroups; ++g) {
+    const int c = g & 1, n = c ^ 1;
+    if (g + 1 < Geo<KB>::kGroups) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[n][i] = frag<T, KB, AK>(As, 128 * wm + 32 * i, g + 1, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[n][i] = frag<T, KB, BK>(Bs, 128 * wn + 32 * i, g + 1, lane);
+    }
+    part(g);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) mma(acc[mi][ni], a[mi], b[ni]);
+      for (int ni = 0; ni < 4; ++ni) mma(acc[mi][ni], a[c][mi], b[c][ni]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Double-buffered main loop over the n stages of one tile.  issue(j, a, b) starts the loads of
-// stage j into LDS buffers (a, b).  Stage j is computed from buffer pair j & 1; the loads of
-// stage j + 1 are in flight while stage j is computed.  The loop has a single exit so the
-// accumulators stay in place across it.
-template <typename T, bool AK, bool BK, typename Issue>
-__device__ __forceinline__ void run_tile(int n, Issue&& issue, char* a0, char* b0, char* a1,
-                                         char* b1, f32x16_t (&acc)[4][4], int wm, int wn,
-                                         int lane) {
-  if (n <= 0) return;
-  issue(0, a0, b0);
-  int j = 0;
-  for (; j + 1 < n; j += 2) {
-    wait_vmcnt0();
-    __syncthreads();
-    issue(j + 1, a1, b1);
-    compute_stage<T, AK, BK>(a0, b0, acc, wm, wn, lane);
-    wait_vmcnt0();
-    __syncthreads();
-    if (j + 2 < n) issue(j + 2, a0, b0);
-    compute_stage<T, AK, BK>(a1, b1, acc, wm, wn, lane);
-  }
-  if (j < n) {
-    wait_vmcnt0();
-    __syncthreads();
-    compute_stage<T, AK, BK>(a0, b0, acc, wm, wn, lane);
+// s_waitcnt vmcnt(n) for a compile-time n (expcnt, lgkmcnt not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// LDS buffers of a pipeline of NST stages: NST distinct objects per operand, so the compiler
+// can tell that the direct-to-LDS loads of one stage never touch the buffers being read.
+template <int NST>
+struct Bufs {
+  char* a[NST];
+  char* b[NST];
+};
+
+// Waits until at most `keep` stages of loads (of this wave) are still in flight.
+template <int KB, int NST>
+__device__ __forceinline__ void wait_stages(int keep) {
+  constexpr int I = 2 * Geo<KB>::kIssue;   // instructions per stage (both operands)
+  if (NST >= 4 && keep >= 2) {
+    wait_vmcnt<(NST >= 4 ? 2 : 0) * I>();
+  } else if (NST >= 3 && keep >= 1) {
+    wait_vmcnt<(NST >= 3 ? 1 : 0) * I>();
+  } else {
+    wait_vmcnt<0>();
   }
 }
 
-// Stages [base, base + n) of a longer stream of `total` stages; n and base are even, so stage
-// g lives in buffer pair g & 1 and every tile starts in pair 0.  Stage base must already be
-// issued; the stage after the last one (if any) is issued before returning, so the next tile
-// starts with its loads in flight.  Straight-line pairs keep the accumulators in place.
-template <typename T, bool AK, bool BK, typename Issue>
-__device__ __forceinline__ void run_stream(int base, int n, int total, Issue&& issue, char* a0,
-                                           char* b0, char* a1, char* b1,
-                                           f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
-  for (int j = 0; j < n; j += 2) {
-    const int g = base + j;
-    wait_vmcnt0();
-    __syncthreads();
-    issue(g + 1, a1, b1);
-    compute_stage<T, AK, BK>(a0, b0, acc, wm, wn, lane);
-    wait_vmcnt0();
-    __syncthreads();
-    if (g + 2 < total) issue(g + 2, a0, b0);
-    compute_stage<T, AK, BK>(a1, b1, acc, wm, wn, lane);
+// Workgroup barrier between pipeline stages.  Each wave has already waited (vmcnt) for its
+// own direct-to-LDS loads of the stage about to be read, and every LDS read of the buffer about
+// to be refilled has been consumed by an MFMA, so no memory fence is needed: __syncthreads()
+// would add one that waits for ALL outstanding loads, including the prefetched stages.  The
+// empty asm statements keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Software pipeline over stages [base, base + n) of a stream of `total` stages; base and n
+// are multiples of NST, so stage g lives in buffer g % NST.  Stages base .. base + NST - 2
+// must already be issued (run_prologue); while stage g is computed, the loads of stages
+// g + 1 .. g + NST - 1 are in flight.  Issuing continues into the next tile of the stream.
+// issue(g) prepares stage g and returns st with st(a, b, p) starting slice p of its loads
+// into LDS buffers (a, b); the slices p = 0 .. KB / 32 - 1 together cover both operands.
+template <typename T, int KB, int NST, bool AK, bool BK, typename Issue>
+__device__ __forceinline__ void run_stream(int base, int n, int total, Issue&& issue,
+                                           const Bufs<NST>& B, f32x16_t (&acc)[4][4], int wm,
+                                           int wn, int lane) {
+  constexpr int P = NST - 1;   // prefetch distance
+  for (int j = 0; j < n; j += NST) {
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+      const int g = base + j + u;
+      // stages issued after g: g + 1 .. min(g + P - 1, total - 1)
+      const int ahead = min(P - 1, total - 1 - g);
+      wait_stages<KB, NST>(ahead);
+      stage_barrier();
+      const bool more = g + P < total;
+      char* const na = B.a[(u + P) % NST];
+      char* const nb = B.b[(u + P) % NST];
+      const auto st = issue(more ? g + P : g);   // per-stage address setup, once
+      compute_stage<T, KB, AK, BK>(B.a[u], B.b[u], acc, wm, wn, lane, [&](int p) {
+        if (more) st(na, nb, p);
+      });
+    }
   }
 }
+
+// Issues the first NST - 1 stages of a stream (fewer if the stream is shorter).
+template <int KB, int NST, typename Issue>
+__device__ __forceinline__ void run_prologue(int total, Issue&& issue, const Bufs<NST>& B) {
+#pragma unroll
+  for (int u = 0; u < NST - 1; ++u)
+    if (u < total) {
+      const auto st = issue(u);
+#pragma unroll
+      for (int p = 0; p < Geo<KB>::kGroups; ++p) st(B.a[u], B.b[u], p);
+    }
+}
+
+// Slice p of a stage covers instructions [p * kPer, (p + 1) * kPer) of each operand.
+template <int KB>
+struct Slices {
+  static constexpr int kPer = Geo<KB>::kIssue / Geo<KB>::kGroups;   // = 2
+};
 
 __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
 #pragma unroll

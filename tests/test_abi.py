@@ -46,8 +46,8 @@ def test_status_strings(lib):
 @pytest.mark.parametrize("dt", [0, 1])
 def test_workspace_has_no_tokens_times_vocabulary_term(lib, dt):
     """Extra device bytes are bounded by a per-token constant that does not grow with V:
-    forward <= 8 bytes x 256 ranges per token, backward <= one chunk of 8192 vocabulary
-    columns of G per (padded) token plus its block flags."""
+    forward <= 8 bytes x 256 ranges per token, backward <= two chunks of 8192 vocabulary
+    columns of G per (padded) token plus their block flags."""
     sz = 4 if dt == 0 else 2
     for V, D in ((256000, 2304), (128256, 4096), (32000, 2048), (1000, 64), (10 ** 6, 64)):
         for N in (1, 255, 4096, 8192, 65536):
@@ -56,12 +56,12 @@ def test_workspace_has_no_tokens_times_vocabulary_term(lib, dt):
             bb = lib.cce_backward_workspace_bytes(N, V, D, dt)
             mb = lib.cce_loss_mean_workspace_bytes(N, V, D, dt)
             assert 0 < fb <= 2048 * N + 256
-            assert 0 < bb <= pad * 8192 * sz + pad * 2 + 512
+            assert 0 < bb <= 2 * (pad * 8192 * sz + pad * 2 + 256)
             assert fb + bb < mb <= fb + bb + 8 * (N + 64) + 512
     # the logits of one config-sized problem would be 4 N V bytes; the workspace is far below
     N, V, D = 8192, 256000, 2304
     total = lib.cce_loss_mean_workspace_bytes(N, V, D, 1)
-    assert total < 4 * N * V / 50
+    assert total < 4 * N * V / 25
 
 
 def test_plan_introspection(lib):
