@@ -95,7 +95,7 @@ def main() -> int:
     ap.add_argument("--filter-eps", type=float, default=None,
                     help="override the workload's gradient filter threshold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times): the reference kernel "
                          "for scaling the HBM byte counters of a profiler")
