@@ -158,7 +158,7 @@ cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, i
   }
   if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   TimedLaunch tl(CCE_KERNEL_FWD_FINISH, st);
-  hipLaunchKernelGGL(k_fwd_finish<T>, dim3((unsigned)ceil_div(N, 4)), dim3(kThreads), 0, st, E,
+  hipLaunchKernelGGL(k_fwd_finish<T>, dim3((unsigned)ceil_div(N, 4)), dim3(kFinishThreads), 0, st, E,
                      C, tgt, (int)N, (int)V, (int)D, (int)n_split, part, ii, loss, lse, err);
   return launch_status();
 }

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
                                                          int D, int n_split, int n_vt,
                                                          int n_items, float2* __restrict__ part) {
   CCE_STAGE_BUFFERS(KB, NST, B)
-  __shared__ float2 sRed[4][128];
+  __shared__ float2 sRed[4][kWaveN];
   constexpr int KS = KB / (int)sizeof(T);
   constexpr int I = Geo<KB>::kIssue;
 
@@ -71,13 +71,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
   const int n_k = padded_stages<T, KB, NST>(D);
   const int iters = (vt1 - vt0) * n_k;
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave_m(wave), wn = wave_n(wave);
   const int tok0 = tb * kTile;
 
-  float m_run[4], s_run[4];
+  float m_run[kNB], s_run[kNB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; s_run[i] = 0.f; }
-  f32x16_t acc[4][4];
+  for (int i = 0; i < kNB; ++i) { m_run[i] = -INFINITY; s_run[i] = 0.f; }
+  Acc acc;
   zero_acc(acc);
 
   const int64_t ldb = (int64_t)D * sizeof(T);
@@ -91,11 +91,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
     const T* ob = E + (int64_t)tok0 * D + k0;
     const int ra = tile_records(V, (int64_t)vt * kTile, ldb, kb);
     const int rb = tile_records(N, tok0, ldb, kb);
-    return [=, &off](char* a, char* b, int p) {
-      const int q0 = p * Slices<KB>::kPer, q1 = q0 + Slices<KB>::kPer;
-      kmajor_issue<KB>(oa, off, ra, kc, a, wave, lane, q0, q1);
-      kmajor_issue<KB>(ob, off, rb, kc, b, wave, lane, q0, q1);
-    };
+    return stage_issue<KB>(
+        [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(oa, off, ra, kc, l, wave, lane, q0, q1); },
+        [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(ob, off, rb, kc, l, wave, lane, q0, q1); });
   };
   // Online log-sum-exp update for the finished tile, one token column group (ni) at a time.
   // Single pass against the running maximum m: t = z log2(e) - m, s += sum 2^t, with eight
@@ -103,13 +101,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
   // rebased to the new maximum.  If some value exceeds the running maximum by more than 2^64
   // (always on the first tile, where m = -inf), the wave recomputes the group exactly.
   auto epilogue = [&](int vt) {
-    const int vbase = vt * kTile + 128 * wm;
+    const int vbase = vt * kTile + kWaveM * wm;
     const bool full = vt * kTile + kTile <= V;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
+    for (int ni = 0; ni < kNB; ++ni) {
       float x[64];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float z = acc[mi][ni][r];
@@ -163,7 +161,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
   // merge the two row halves of each column (lanes l and l ^ 32), then the two waves that
   // share columns (wm = 0, 1) through LDS
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+  for (int ni = 0; ni < kNB; ++ni) {
     const float mo = __shfl_xor(m_run[ni], 32);
     const float so = __shfl_xor(s_run[ni], 32);
     const float mn = fmaxf(m_run[ni], mo);
@@ -173,17 +171,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
   }
   if (wm == 1 && lane < 32) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) sRed[wn][32 * ni + lane] = make_float2(m_run[ni], s_run[ni]);
+    for (int ni = 0; ni < kNB; ++ni) sRed[wn][32 * ni + lane] = make_float2(m_run[ni], s_run[ni]);
   }
   __syncthreads();
   if (wm == 0 && lane < 32) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
+    for (int ni = 0; ni < kNB; ++ni) {
       const float2 o = sRed[wn][32 * ni + lane];
       const float mn = fmaxf(m_run[ni], o.x);
       const float mu = mn == -INFINITY ? 0.f : mn;
       const float s = s_run[ni] * exp2_fast(m_run[ni] - mu) + o.y * exp2_fast(o.x - mu);
-      const int n = tok0 + 128 * wn + 32 * ni + lane;
+      const int n = tok0 + kWaveN * wn + 32 * ni + lane;
       if (n < N) part[(int64_t)sp * N + n] = make_float2(mn, s);
     }
   }
@@ -204,8 +202,10 @@ __device__ __forceinline__ float wave_max(float v) {
 // Forward finish: one wave per token.  LSE = ln2 * (M + log2 sum_i s_i 2^(m_i - M)); the
 // target logit is a gather-dot of E[n] with C[t[n]] in fp32; loss = LSE - z_t.
 // ------------------------------------------------------------------------------------------
+constexpr int kFinishThreads = 256;   // 4 tokens per workgroup, one wave each
+
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_fwd_finish(
+__global__ __launch_bounds__(kFinishThreads) void k_fwd_finish(
     const T* __restrict__ E, const T* __restrict__ C, const int64_t* __restrict__ tgt, int N,
     int V, int D, int n_split, const float2* __restrict__ part, int64_t ignore_index,
     float* __restrict__ loss, float* __restrict__ lse, int32_t* __restrict__ err) {
@@ -296,12 +296,12 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
   grouped_tile(lin, n_vtc, tb, vt);
   if (tb >= n_tb || vt >= n_vtc) return;
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave_m(wave), wn = wave_n(wave);
   const int tok0 = tb * kTile, vl0 = vt * kTile;  // vl0: chunk-local first vocab row
   const int n_k = padded_stages<T, KB, NST>(D);
   const T* Cc = C + (int64_t)v0 * D;
 
-  f32x16_t acc[4][4];
+  Acc acc;
   zero_acc(acc);
   const int64_t ldb = (int64_t)D * sizeof(T);
   uint32_t off[I];
@@ -314,19 +314,17 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
     const T* ob = E + (int64_t)tok0 * D + k0;
     const int ra = tile_records(vc, vl0, ldb, kb);
     const int rb = tile_records(N, tok0, ldb, kb);
-    return [=, &off](char* a, char* b, int p) {
-      const int q0 = p * Slices<KB>::kPer, q1 = q0 + Slices<KB>::kPer;
-      kmajor_issue<KB>(oa, off, ra, kc, a, wave, lane, q0, q1);
-      kmajor_issue<KB>(ob, off, rb, kc, b, wave, lane, q0, q1);
-    };
+    return stage_issue<KB>(
+        [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(oa, off, ra, kc, l, wave, lane, q0, q1); },
+        [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(ob, off, rb, kc, l, wave, lane, q0, q1); });
   };
   // per column (token) constants, loaded before the main loop so their latency is hidden
-  float coef[4], lse2[4];
-  int trow[4];
-  bool valid[4];
+  float coef[kNB], lse2[kNB];
+  int trow[kNB];
+  bool valid[kNB];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int n = tok0 + 128 * wn + 32 * ni + (lane & 31);
+  for (int ni = 0; ni < kNB; ++ni) {
+    const int n = tok0 + kWaveN * wn + 32 * ni + (lane & 31);
     bool ok = false;
     float w = 0.f, l2 = 0.f;
     int tr = -1;
@@ -335,7 +333,7 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
       ok = t != ignore_index;
       w = dloss[(int64_t)n * dstride];
       l2 = lse[n] * kLog2e;
-      const int64_t tl = t - (int64_t)v0 - vl0 - 128 * wm;  // target row within this wave's rows
+      const int64_t tl = t - (int64_t)v0 - vl0 - kWaveM * wm;  // target row within the wave's rows
       tr = (ok && tl >= 0 && tl < 128) ? (int)tl : -1;
     }
     valid[ni] = ok;
@@ -351,66 +349,62 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
   // 64 x 64 block the largest p (independent maxima, no serial chains)
   const bool filter = eps > 0.f;
   const bool full = vl0 + kTile <= vc;
-  float pmax[2][4];
+  float pmax[2][kNB];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) pmax[a][ni] = 0.f;
+    for (int ni = 0; ni < kNB; ++ni) pmax[a][ni] = 0.f;
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
+  for (int ni = 0; ni < kNB; ++ni)
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * mi + acc_row(r, lane);  // row within this wave's 128 rows
         float p = exp2_fast(__builtin_fmaf(acc[mi][ni][r], kLog2e, -lse2[ni]));
-        if (!full && vl0 + 128 * wm + row >= vc) p = 0.f;
+        if (!full && vl0 + kWaveM * wm + row >= vc) p = 0.f;
         pmax[mi >> 1][ni] = fmaxf(pmax[mi >> 1][ni], p);
         acc[mi][ni][r] = __builtin_fmaf(coef[ni], p, row == trow[ni] ? -coef[ni] : 0.f);
       }
-  bool sig[2][2];
+  // the wave's 64 token columns are one filter block wide; its 128 vocabulary rows two blocks
+  bool sig[2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 2; ++a) {
+    bool any = false;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      bool any = false;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int ni = 2 * b + h;
-        const bool has_t = trow[ni] >= 64 * a && trow[ni] < 64 * a + 64;
-        any |= valid[ni] && (pmax[a][ni] >= eps || has_t);
-      }
-      sig[a][b] = any;
+    for (int ni = 0; ni < kNB; ++ni) {
+      const bool has_t = trow[ni] >= 64 * a && trow[ni] < 64 * a + 64;
+      any |= valid[ni] && (pmax[a][ni] >= eps || has_t);
     }
+    sig[a] = any;
+  }
 
   // block decisions (wave-wide), flags, statistics
   int n_skipped = 0;
-  bool keep[2][2];
+  bool keep[2];
+  const int nblk = tok0 + kWaveN * wn;          // token start of the wave's block
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int vblk = vl0 + 128 * wm + 64 * a;   // chunk-local vocab start of the block
-      const int nblk = tok0 + 128 * wn + 64 * b;  // token start of the block
-      const bool in_range = vblk < vc && nblk < N;
-      const bool any = __ballot(sig[a][b]) != 0ull;
-      const bool k = in_range && (!filter || any);
-      keep[a][b] = k;
-      if (in_range && !k) ++n_skipped;
-      if (lane == 0) flags[(int64_t)(nblk >> 6) * fstride + (vblk >> 6)] = k ? 0 : 1;
-    }
+  for (int a = 0; a < 2; ++a) {
+    const int vblk = vl0 + kWaveM * wm + 64 * a;  // chunk-local vocab start of the block
+    const bool in_range = vblk < vc && nblk < N;
+    const bool any = __ballot(sig[a]) != 0ull;
+    const bool k = in_range && (!filter || any);
+    keep[a] = k;
+    if (in_range && !k) ++n_skipped;
+    if (lane == 0) flags[(int64_t)(nblk >> 6) * fstride + (vblk >> 6)] = k ? 0 : 1;
+  }
   if (skip_count && lane == 0 && n_skipped) atomicAdd(skip_count, (unsigned long long)n_skipped);
 
   // store the kept blocks: 4 consecutive vocab rows of one token per lane and register group
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      if (!keep[mi >> 1][ni >> 1]) continue;
-      const int n = tok0 + 128 * wn + 32 * ni + (lane & 31);
+    for (int ni = 0; ni < kNB; ++ni) {
+      if (!keep[mi >> 1]) continue;
+      const int n = tok0 + kWaveN * wn + 32 * ni + (lane & 31);
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int vloc = vl0 + 128 * wm + 32 * mi + 8 * rq + 4 * (lane >> 5);
+        const int vloc = vl0 + kWaveM * wm + 32 * mi + 8 * rq + 4 * (lane >> 5);
         T* dst = G + (int64_t)n * ldg + vloc;
         if constexpr (sizeof(T) == 2) {
           typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
@@ -428,27 +422,27 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
     }
 }
 
-// Writes (or adds) this wave's 128 x 128 accumulators to a row-major fp32 matrix out[rows][ld]
+// Writes (or adds) this wave's 128 x 64 accumulators to a row-major fp32 matrix out[rows][ld]
 // at (row0, col0); rows >= row_lim and columns >= col_lim are dropped.  For each register a
 // half-wave writes 32 consecutive columns (128 bytes).
 __device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, int row0,
-                                           int row_lim, int col0, int col_lim,
-                                           f32x16_t (&acc)[4][4], int lane, bool add) {
-  const bool full = row0 + 128 <= row_lim && col0 + 128 <= col_lim;
+                                           int row_lim, int col0, int col_lim, Acc& acc,
+                                           int lane, bool add) {
+  const bool full = row0 + kWaveM <= row_lim && col0 + kWaveN <= col_lim;
   if (full && !add) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < kNB; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           out[(int64_t)(row0 + 32 * mi + acc_row(r, lane)) * ld + col0 + 32 * ni + (lane & 31)] =
               acc[mi][ni][r];
   } else if (full) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < kNB; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float* p =
@@ -457,9 +451,9 @@ __device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, 
         }
   } else {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < kNB; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = row0 + 32 * mi + acc_row(r, lane), col = col0 + 32 * ni + (lane & 31);
@@ -503,7 +497,8 @@ __device__ __forceinline__ int build_stage_list(const uint8_t* __restrict__ flag
     for (int w = 0; w < wave; ++w) off += wave_cnt[w];
     const int before = __popcll(bal & ((1ull << lane) - 1ull));
     if (active) list[off + before] = (s << 4) | (int)mask;
-    total += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) total += wave_cnt[w];
     __syncthreads();
   }
   // pad to a multiple of NST with all-zero stages (every block masked), so the pipeline runs
@@ -538,13 +533,13 @@ __device__ __forceinline__ void tile_bwd_de(const BwdArgs<T>& A, int lin, const 
   grouped_tile(lin, n_dt, tb, dt);
   if (tb >= n_tb || dt >= n_dt) return;
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave_m(wave), wn = wave_n(wave);
   const int tok0 = tb * kTile, d0 = dt * kTile;
   const int n_stages = kv / KS;
   const int n_act =
       build_stage_list<KS, NST>(flags, fstride, n_stages, true, tb * 4, sList, sCnt);
 
-  f32x16_t acc[4][4];
+  Acc acc;
   zero_acc(acc);
   if (n_act == 0 && accumulate) return;
   const int64_t ldb = (int64_t)D * sizeof(T);
@@ -554,22 +549,22 @@ __device__ __forceinline__ void tile_bwd_de(const BwdArgs<T>& A, int lin, const 
   auto issue = [&](int i) {
     const int e = __builtin_amdgcn_readfirstlane(sList[i]);
     const int k0 = (e >> 4) * KS;
-    const bool zero = (e >> wave) & 1;  // wave w loads the tile's token rows 64 w .. 64 w + 63
+    const bool zero = (e >> (wave >> 1)) & 1;  // wave w loads token rows 32 w .. 32 w + 31
     const T* oa = G + (int64_t)tok0 * ldg + k0;
     const T* ob = Cc + (int64_t)k0 * D + d0;
     const int ra = zero ? 0 : kRecords;
     const int rb = tile_records(vc, k0, ldb, (int64_t)d0 * sizeof(T));
-    return [=, &offA, &offB](char* a, char* b, int p) {
-      const int q0 = p * Slices<KB>::kPer, q1 = q0 + Slices<KB>::kPer;
-      kmajor_issue<KB>(oa, offA, ra, Geo<KB>::kChunks, a, wave, lane, q0, q1);
-      mn_issue<T, KB>(ob, offB, rb, 0u, b, wave, lane, q0, q1);
-    };
+    return stage_issue<KB>(
+        [=, &offA](char* l, int q0, int q1) {
+          kmajor_issue<KB>(oa, offA, ra, Geo<KB>::kChunks, l, wave, lane, q0, q1);
+        },
+        [=, &offB](char* l, int q0, int q1) { mn_issue<T, KB>(ob, offB, rb, 0u, l, wave, lane, q0, q1); });
   };
   if (n_act > 0) {
     run_prologue<KB, NST>(n_act, issue, B);
     run_stream<T, KB, NST, true, false>(0, n_act, n_act, issue, B, acc, wm, wn, lane);
   }
-  store_tile(dE, D, tok0 + 128 * wm, N, d0 + 128 * wn, D, acc, lane, accumulate != 0);
+  store_tile(dE, D, tok0 + kWaveM * wm, N, d0 + kWaveN * wn, D, acc, lane, accumulate != 0);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -595,14 +590,14 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
   grouped_tile(lin, n_dt, vt, dt);
   if (vt >= n_vtc || dt >= n_dt) return;
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave_m(wave), wn = wave_n(wave);
   const int vl0 = vt * kTile, d0 = dt * kTile;
   const int n_stages = n_pad / KS;
   const int64_t ldb = (int64_t)D * sizeof(T);
   uint32_t offA[I], offB[I];
   mn_offsets<T, KB>(offA, ldg * (int64_t)sizeof(T), vl0, (int)ldg, wave, lane);
   mn_offsets<T, KB>(offB, ldb, d0, D, wave, lane);
-  f32x16_t acc[4][4];
+  Acc acc;
   zero_acc(acc);
   for (int sbase = 0; sbase < n_stages; sbase += kPiece) {
     const int cnt = min(kPiece, n_stages - sbase);
@@ -615,11 +610,11 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
       const T* ob = E + (int64_t)k0 * D + d0;
       const uint32_t zc = (uint32_t)(e & 15);
       const int rb = tile_records(N, k0, ldb, (int64_t)d0 * sizeof(T));
-      return [=, &offA, &offB](char* a, char* b, int p) {
-        const int q0 = p * Slices<KB>::kPer, q1 = q0 + Slices<KB>::kPer;
-        mn_issue<T, KB>(oa, offA, kRecords, zc, a, wave, lane, q0, q1);
-        mn_issue<T, KB>(ob, offB, rb, 0u, b, wave, lane, q0, q1);
-      };
+      return stage_issue<KB>(
+          [=, &offA](char* l, int q0, int q1) {
+            mn_issue<T, KB>(oa, offA, kRecords, zc, l, wave, lane, q0, q1);
+          },
+          [=, &offB](char* l, int q0, int q1) { mn_issue<T, KB>(ob, offB, rb, 0u, l, wave, lane, q0, q1); });
     };
     if (n_act > 0) {
       run_prologue<KB, NST>(n_act, issue, B);
@@ -627,7 +622,7 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
     }
     __syncthreads();
   }
-  store_tile(dCc, D, vl0 + 128 * wm, vc, d0 + 128 * wn, D, acc, lane, false);
+  store_tile(dCc, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc, lane, false);
 }
 
 // Work items of the backward launches, in super-blocks of 4 x 8 tiles.
@@ -652,7 +647,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_fused(BwdArgs<T> A, BwdArgs
                                                            int r_de, int r_dc) {
   CCE_STAGE_BUFFERS(KB, NST, B)
   __shared__ int sList[kDcPiece + NST];
-  __shared__ int sCnt[4];
+  __shared__ int sCnt[kWaves];
   const int b = blockIdx.x;
   if (b < r_de) {
     tile_bwd_de<T, KB, NST>(A, xcd_remap(b, r_de), B, sList, sCnt);

@@ -1,12 +1,14 @@
 // Tile engine for the Cut Cross-Entropy kernels on gfx950 (MI355X, CDNA4).
 //
 // Every hot kernel of the library is a 256 x 256 output tile of a matrix product
-// acc[m][n] = sum_k A[m][k] B[n][k] computed by one workgroup of 256 threads (4 waves of 64):
-//   * each wave owns a 128 x 128 quarter as 4 x 4 blocks of 32 x 32 fp32 accumulators
-//     (v_mfma_f32_32x32x16_bf16 for bf16 operands, v_mfma_f32_32x32x2f32 for fp32);
+// acc[m][n] = sum_k A[m][k] B[n][k] computed by one workgroup of 512 threads (8 waves of 64,
+// two per SIMD, so one wave's MFMAs cover the other's LDS, barrier and load waits):
+//   * wave w owns rows 128 (w / 4) .. + 127 and columns 64 (w % 4) .. + 63 as 4 x 2 blocks of
+//     32 x 32 fp32 accumulators (v_mfma_f32_32x32x16_bf16 for bf16 operands,
+//     v_mfma_f32_32x32x2f32 for fp32);
 //   * operands stream HBM -> LDS with direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds),
-//     one stage of 128 bytes of K per operand row, double buffered in two separate LDS
-//     objects so the loads of stage s+1 overlap the MFMAs of stage s;
+//     one stage of KB bytes of K per operand row, NST stages in NST separate LDS objects so the
+//     loads of later stages overlap the MFMAs of the current one;
 //   * an operand is either K-major (row = m or n, K contiguous, e.g. E[N,D] and C[V,D] when
 //     contracting over D) or MN-major (row = k, m/n contiguous, e.g. C when contracting over
 //     the vocabulary).  K-major fragments are read with ds_read_b128, MN-major bf16 fragments
@@ -30,41 +32,49 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 256;           // tile rows (M) and columns (N)
+constexpr int kWaveM = 128;          // rows of a wave's accumulator tile
+constexpr int kWaveN = 64;           // columns of a wave's accumulator tile
+constexpr int kMB = kWaveM / 32;     // 32 x 32 blocks per wave along M
+constexpr int kNB = kWaveN / 32;     // ... along N
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+typedef f32x16_t Acc[kMB][kNB];
 
 template <typename T> struct Traits;
 template <> struct Traits<__bf16> {
   static constexpr int kEpc = 8;     // elements per 16-byte chunk
-  static constexpr int kKs = 64;     // K per stage (128 bytes per K-major row)
   typedef bf16x8_t frag_t;
 };
 template <> struct Traits<float> {
   static constexpr int kEpc = 4;
-  static constexpr int kKs = 32;
   typedef f32x4_t frag_t;
 };
 
-__device__ __forceinline__ void wait_vmcnt0() {
-  // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima (no wait)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
-// Wave index as a scalar (uniform) value.
+// Wave index as a scalar (uniform) value, and the wave's place in the tile.
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
+__device__ __forceinline__ int wave_m(int wave) { return wave >> 2; }
+__device__ __forceinline__ int wave_n(int wave) { return wave & 3; }
+
+// s_waitcnt vmcnt(n) for a compile-time n (expcnt, lgkmcnt not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // ---------------------------------------------------------------------------------------
-// HBM -> LDS stage loads with buffer_load ... lds.  Each wave issues 8 instructions per
-// operand; one instruction moves 64 lanes x 16 bytes into 1 KB of consecutive LDS.  Every
-// lane keeps a fixed byte offset per instruction relative to the stage's tile origin (a
-// uniform pointer turned into a buffer descriptor); masked lanes use an offset past the
-// descriptor's range, which the hardware answers with zeros.  The XOR swizzles make the
-// fragment reads below free of bank conflicts: a lane picks which global chunk lands in its
-// fixed LDS slot.
+// HBM -> LDS stage loads with buffer_load ... lds.  One instruction moves 64 lanes x 16 bytes
+// into 1 KB of consecutive LDS.  Every lane keeps a fixed byte offset per instruction relative
+// to the stage's tile origin (a uniform pointer turned into a buffer descriptor); masked lanes
+// use an offset past the descriptor's range, which the hardware answers with zeros.  The XOR
+// swizzles make the fragment reads below free of bank conflicts: a lane picks which global
+// chunk lands in its fixed LDS slot.
 // ---------------------------------------------------------------------------------------
 constexpr uint32_t kOob = 0x80000000u;         // offset answered with zeros
 constexpr int kRecords = 0x7FFFFFF0;           // descriptor range
@@ -77,24 +87,23 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* lds, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
 }
 
-// Stage geometry.  KB = bytes of K per K-major operand row per stage (128 or 64), so one
-// operand's share of a stage is 256 x KB bytes, and each wave issues KB / 16 direct-to-LDS
-// instructions per operand and stage.
+// Stage geometry.  KB = bytes of K per K-major operand row per stage (128 or 64): one
+// operand's share of a stage is 256 x KB bytes = KB / 4 instructions of 1 KB, KB / 32 per wave.
 template <int KB>
 struct Geo {
   static_assert(KB == 128 || KB == 64, "stage K bytes");
-  static constexpr int kChunks = KB / 16;         // 16-byte chunks per K-major row
-  static constexpr int kIssue = KB / 16;          // instructions per wave per operand
-  static constexpr int kRowsPerWin = 256 / KB;    // K-major rows per 256-byte bank window
-  static constexpr int kOpBytes = 256 * KB;       // one operand's share of one stage
-  static constexpr int kGroups = KB / 32;         // MFMA k-groups per stage
+  static constexpr int kChunks = KB / 16;                 // 16-byte chunks per K-major row
+  static constexpr int kIssue = 256 * KB / 1024 / kWaves; // instructions per wave per operand
+  static constexpr int kRowsPerWin = 256 / KB;            // K-major rows per 256-byte window
+  static constexpr int kOpBytes = 256 * KB;               // one operand's share of one stage
+  static constexpr int kGroups = KB / 32;                 // MFMA k-groups per stage
 };
 
 // K-major operand: 256 rows x KB bytes per stage.  LDS slot (row r, chunk pc) holds logical K
 // chunk pc ^ f(r), f(r) = (r / rows-per-window) mod chunks, which spreads the 16 rows read by
-// one quarter-wave over distinct banks.  Instruction q of wave w fills 1 KB of consecutive
-// LDS, i.e. rows (w * I + q) * (1024 / KB) onwards (I = instructions per wave), so wave w
-// covers rows 64 w .. 64 w + 63.
+// one quarter-wave over distinct banks.  Instruction q of wave w fills rows
+// (w * I + q) * (1024 / KB) onwards (I instructions per wave), so wave w covers the 32 rows
+// 32 w .. 32 w + 31.
 template <int KB>
 __device__ __forceinline__ int kmajor_row(int wave, int q, int lane) {
   return (wave * Geo<KB>::kIssue + q) * (1024 / KB) + lane / Geo<KB>::kChunks;
@@ -124,8 +133,8 @@ __device__ __forceinline__ int tile_records(int64_t row_lim, int64_t row0, int64
   return b <= 0 ? 0 : (b > kRecords ? kRecords : (int)b);
 }
 
-// One slice of a stage: instructions [Q0, Q1) of this wave.  k_chunks = valid 16-byte K
-// chunks left from k0 (>= chunks per row: full stage).
+// Instructions [q0, q1) of this wave's share of a stage.  k_chunks = valid 16-byte K chunks
+// left from k0 (>= chunks per row: full stage).
 template <int KB>
 __device__ __forceinline__ void kmajor_issue(const void* origin,
                                              const uint32_t (&off)[Geo<KB>::kIssue], int records,
@@ -169,8 +178,7 @@ __device__ __forceinline__ void mn_offsets(uint32_t (&off)[Geo<KB>::kIssue], int
   }
 }
 
-// One slice of a stage: instructions [Q0, Q1).  zero_cols bit b = load zeros for columns
-// 64 b .. 64 b + 63 of the tile.
+// Instructions [q0, q1).  zero_cols bit b = load zeros for columns 64 b .. 64 b + 63.
 template <typename T, int KB>
 __device__ __forceinline__ void mn_issue(const void* origin, const uint32_t (&off)[Geo<KB>::kIssue],
                                          int records, uint32_t zero_cols, char* lds, int wave,
@@ -183,6 +191,30 @@ __device__ __forceinline__ void mn_issue(const void* origin, const uint32_t (&of
     if (zero_cols) o = ((zero_cols >> (mn_col<T, KB>(wave, q, lane) >> 6)) & 1u) ? kOob : o;
     lds_load16(rs, lds + (wave * Geo<KB>::kIssue + q) * 1024, o);
   }
+}
+
+// The loads of one stage: fa(lds, q0, q1) / fb(lds, q0, q1) issue instructions [q0, q1) of
+// operand A / B into the given LDS buffer.
+template <int KB, typename FA, typename FB>
+struct StageIssue {
+  FA fa;
+  FB fb;
+  __device__ __forceinline__ void operator()(char* a, char* b, int q0, int q1) const {
+    fa(a, q0, q1);
+    fb(b, q0, q1);
+  }
+  // instruction j of the stage's 2 x I: those of operand A first
+  __device__ __forceinline__ void one(char* a, char* b, int j) const {
+    constexpr int I = Geo<KB>::kIssue;
+    if (j < I)
+      fa(a, j, j + 1);
+    else
+      fb(b, j - I, j - I + 1);
+  }
+};
+template <int KB, typename FA, typename FB>
+__device__ __forceinline__ StageIssue<KB, FA, FB> stage_issue(FA fa, FB fb) {
+  return StageIssue<KB, FA, FB>{fa, fb};
 }
 
 // ---------------------------------------------------------------------------------------
@@ -247,69 +279,55 @@ __device__ __forceinline__ void mma(f32x16_t& acc, const f32x4_t& a, const f32x4
   for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], acc, 0, 0, 0);
 }
 
-// One stage of MFMAs for this wave: KB / 32 k-groups x 4 x 4 blocks.  Before the MFMAs of
-// k-group g it reads the fragments of group g + 1 from LDS and calls part(g), which issues
-// slice g of a later stage's direct-to-LDS loads; spreading the loads over the stage keeps
-// the address units from stalling the MFMA issue.  The scheduling barriers keep the compiler
-// from regrouping the reads, loads and MFMAs.
 struct NoIssue {
-  __device__ __forceinline__ void operator()(int) const {}
+  __device__ __forceinline__ void one(int) const {}
 };
 
+// One stage of MFMAs for this wave: KB / 32 k-groups x 4 x 2 blocks.  While the 8 MFMAs of the
+// first k-group run, part.one(j) issues the j-th load of a later stage, one after each MFMA,
+// so the address units never stall the MFMA issue and the loads get the rest of the stage to
+// land.  K-major fragments of group g + 1 are read while group g runs.  Transposing LDS reads
+// carry no alias information for the compiler, which would make each of them wait for every
+// direct-to-LDS load in flight, so with an MN-major operand all fragments of the stage are
+// read before the loads are issued.  Scheduling barriers keep this order.
 template <typename T, int KB, bool AK, bool BK, typename Part = NoIssue>
-__device__ __forceinline__ void compute_stage(const char* As, const char* Bs,
-                                              f32x16_t (&acc)[4][4], int wm, int wn, int lane,
-                                              Part&& part = Part()) {
+__device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Acc& acc, int wm,
+                                              int wn, int lane, const Part& part = Part()) {
   typedef typename Traits<T>::frag_t F;
-  F a[2][4], b[2][4];
+  constexpr int G = Geo<KB>::kGroups;
+  constexpr bool kEarly = sizeof(T) == 2 && (!AK || !BK);
+  constexpr int S = kEarly ? G : 2;
+  F a[S][kMB], b[S][kNB];
+  auto read = [&](int slot, int g) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[0][i] = frag<T, KB, AK>(As, 128 * wm + 32 * i, 0, lane);
+    for (int i = 0; i < kMB; ++i) a[slot][i] = frag<T, KB, AK>(As, kWaveM * wm + 32 * i, g, lane);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) b[0][i] = frag<T, KB, BK>(Bs, 128 * wn + 32 * i, 0, lane);
+    for (int i = 0; i < kNB; ++i) b[slot][i] = frag<T, KB, BK>(Bs, kWaveN * wn + 32 * i, g, lane);
+  };
+  if constexpr (kEarly) {
 #pragma unroll
-  for (int g = 0; g < Geo<KB>::kGroups; ++g) {
-    const int c = g & 1, n = c ^ 1;
-    if (g + 1 < Geo<KB>::kGroups) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[n][i] = frag<T, KB, AK>(As, 128 * wm + 32 * i, g + 1, lane);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) b[n][i] = frag<T, KB, BK>(Bs, 128 * wn + 32 * i, g + 1, lane);
-    }
-    part(g);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) mma(acc[mi][ni], a[c][mi], b[c][ni]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// s_waitcnt vmcnt(n) for a compile-time n (expcnt, lgkmcnt not waited for).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// LDS buffers of a pipeline of NST stages: NST distinct objects per operand, so the compiler
-// can tell that the direct-to-LDS loads of one stage never touch the buffers being read.
-template <int NST>
-struct Bufs {
-  char* a[NST];
-  char* b[NST];
-};
-
-// Waits until at most `keep` stages of loads (of this wave) are still in flight.
-template <int KB, int NST>
-__device__ __forceinline__ void wait_stages(int keep) {
-  constexpr int I = 2 * Geo<KB>::kIssue;   // instructions per stage (both operands)
-  if (NST >= 4 && keep >= 2) {
-    wait_vmcnt<(NST >= 4 ? 2 : 0) * I>();
-  } else if (NST >= 3 && keep >= 1) {
-    wait_vmcnt<(NST >= 3 ? 1 : 0) * I>();
+    for (int g = 0; g < G; ++g) read(g, g);
   } else {
-    wait_vmcnt<0>();
+    read(0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int c = kEarly ? g : (g & 1);
+    if constexpr (!kEarly) {
+      if (g + 1 < G) read((g + 1) & 1, g + 1);
+    }
+#pragma unroll
+    for (int mi = 0; mi < kMB; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNB; ++ni) {
+        mma(acc[mi][ni], a[c][mi], b[c][ni]);
+        if (g == 0) {
+          part.one(kNB * mi + ni);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -324,16 +342,36 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// LDS buffers of a pipeline of NST stages: NST distinct objects per operand, so the compiler
+// can tell that the direct-to-LDS loads of one stage never touch the buffers being read.
+template <int NST>
+struct Bufs {
+  char* a[NST];
+  char* b[NST];
+};
+
+// Waits until at most `keep` stages of this wave's loads are still in flight.
+template <int KB, int NST>
+__device__ __forceinline__ void wait_stages(int keep) {
+  constexpr int I = 2 * Geo<KB>::kIssue;   // instructions per stage (both operands)
+  if (NST >= 4 && keep >= 2) {
+    wait_vmcnt<(NST >= 4 ? 2 : 0) * I>();
+  } else if (NST >= 3 && keep >= 1) {
+    wait_vmcnt<(NST >= 3 ? 1 : 0) * I>();
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 // Software pipeline over stages [base, base + n) of a stream of `total` stages; base and n
 // are multiples of NST, so stage g lives in buffer g % NST.  Stages base .. base + NST - 2
 // must already be issued (run_prologue); while stage g is computed, the loads of stages
 // g + 1 .. g + NST - 1 are in flight.  Issuing continues into the next tile of the stream.
-// issue(g) prepares stage g and returns st with st(a, b, p) starting slice p of its loads
-// into LDS buffers (a, b); the slices p = 0 .. KB / 32 - 1 together cover both operands.
+// issue(g) prepares stage g and returns a StageIssue for it.
 template <typename T, int KB, int NST, bool AK, bool BK, typename Issue>
 __device__ __forceinline__ void run_stream(int base, int n, int total, Issue&& issue,
-                                           const Bufs<NST>& B, f32x16_t (&acc)[4][4], int wm,
-                                           int wn, int lane) {
+                                           const Bufs<NST>& B, Acc& acc, int wm, int wn,
+                                           int lane) {
   constexpr int P = NST - 1;   // prefetch distance
   for (int j = 0; j < n; j += NST) {
 #pragma unroll
@@ -347,9 +385,16 @@ __device__ __forceinline__ void run_stream(int base, int n, int total, Issue&& i
       char* const na = B.a[(u + P) % NST];
       char* const nb = B.b[(u + P) % NST];
       const auto st = issue(more ? g + P : g);   // per-stage address setup, once
-      compute_stage<T, KB, AK, BK>(B.a[u], B.b[u], acc, wm, wn, lane, [&](int p) {
-        if (more) st(na, nb, p);
-      });
+      struct Part {
+        const decltype(st)& st;
+        bool more;
+        char* na;
+        char* nb;
+        __device__ __forceinline__ void one(int j) const {
+          if (more && j < 2 * Geo<KB>::kIssue) st.one(na, nb, j);
+        }
+      } part{st, more, na, nb};
+      compute_stage<T, KB, AK, BK>(B.a[u], B.b[u], acc, wm, wn, lane, part);
     }
   }
 }
@@ -361,22 +406,15 @@ __device__ __forceinline__ void run_prologue(int total, Issue&& issue, const Buf
   for (int u = 0; u < NST - 1; ++u)
     if (u < total) {
       const auto st = issue(u);
-#pragma unroll
-      for (int p = 0; p < Geo<KB>::kGroups; ++p) st(B.a[u], B.b[u], p);
+      st(B.a[u], B.b[u], 0, Geo<KB>::kIssue);
     }
 }
 
-// Slice p of a stage covers instructions [p * kPer, (p + 1) * kPer) of each operand.
-template <int KB>
-struct Slices {
-  static constexpr int kPer = Geo<KB>::kIssue / Geo<KB>::kGroups;   // = 2
-};
-
-__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
+__device__ __forceinline__ void zero_acc(Acc& acc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kMB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kNB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
