@@ -143,6 +143,12 @@ struct TimedLaunch {
 
 int grid_for(int64_t items) { return (int)(ceil_div(items, 8) * 8); }
 
+// Whether D leaves a partial group of NST stages of K (then the kernels mask K per lane).
+template <typename T>
+bool k_tail(int64_t D) {
+  return D % ((int64_t)kNST * kKB / (int64_t)sizeof(T)) != 0;
+}
+
 template <typename T>
 cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, int64_t V,
                         int64_t D, int64_t ii, float* loss, float* lse, void* ws, int32_t* err,
@@ -152,9 +158,13 @@ cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, i
   const int64_t items = n_tb * n_split;
   float2* part = (float2*)ws;
   {
-  TimedLaunch tl(CCE_KERNEL_FWD_LSE, st);
-  hipLaunchKernelGGL((k_fwd_lse<T, kKB, kNST>), dim3(grid_for(items)), dim3(kThreads), 0, st, E, C, (int)N,
-                     (int)V, (int)D, (int)n_split, (int)n_vt, (int)items, part);
+    TimedLaunch tl(CCE_KERNEL_FWD_LSE, st);
+    if (k_tail<T>(D))
+      hipLaunchKernelGGL((k_fwd_lse<T, kKB, kNST, true>), dim3(grid_for(items)), dim3(kThreads), 0,
+                         st, E, C, (int)N, (int)V, (int)D, (int)n_split, (int)n_vt, (int)items, part);
+    else
+      hipLaunchKernelGGL((k_fwd_lse<T, kKB, kNST, false>), dim3(grid_for(items)), dim3(kThreads), 0,
+                         st, E, C, (int)N, (int)V, (int)D, (int)n_split, (int)n_vt, (int)items, part);
   }
   if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   TimedLaunch tl(CCE_KERNEL_FWD_FINISH, st);
@@ -199,8 +209,11 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
   {
     const BwdArgs<T> A0 = args(0);
     TimedLaunch tl(CCE_KERNEL_BWD_G, st);
-    hipLaunchKernelGGL((k_bwd_g<T, kKB, kNST>), dim3(grid_for(bwd_items(A0.n_tb, A0.n_vtc))),
-                       dim3(kThreads), 0, st, A0);
+    const dim3 grid(grid_for(bwd_items(A0.n_tb, A0.n_vtc)));
+    if (k_tail<T>(D))
+      hipLaunchKernelGGL((k_bwd_g<T, kKB, kNST, true>), grid, dim3(kThreads), 0, st, A0);
+    else
+      hipLaunchKernelGGL((k_bwd_g<T, kKB, kNST, false>), grid, dim3(kThreads), 0, st, A0);
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   }
   for (int64_t c = 0; c < n_chunks; ++c) {
@@ -211,8 +224,13 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
     const int r_dc = grid_for(bwd_items(A.n_vtc, A.n_dt));
     const int r_g = more ? grid_for(bwd_items(Nx.n_tb, Nx.n_vtc)) : 0;
     TimedLaunch tl(CCE_KERNEL_BWD_FUSED, st);
-    hipLaunchKernelGGL((k_bwd_fused<T, kKB, kNST>), dim3(r_de + r_dc + r_g), dim3(kThreads), 0,
-                       st, A, Nx, r_de, r_dc);
+    const dim3 grid(r_de + r_dc + r_g);
+    if (k_tail<T>(D))
+      hipLaunchKernelGGL((k_bwd_fused<T, kKB, kNST, true>), grid, dim3(kThreads), 0, st, A, Nx,
+                         r_de, r_dc);
+    else
+      hipLaunchKernelGGL((k_bwd_fused<T, kKB, kNST, false>), grid, dim3(kThreads), 0, st, A, Nx,
+                         r_de, r_dc);
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   }
   return CCE_OK;

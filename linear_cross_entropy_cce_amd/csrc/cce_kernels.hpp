@@ -53,7 +53,9 @@ __host__ __device__ constexpr int padded_stages(int K) {
 // Forward: per (token tile, vocabulary range) partial log-sum-exp in base 2.
 //   part[split * N + n] = (m, s): m = max_v z*log2(e) over the range, s = sum 2^(z*log2(e) - m)
 // ------------------------------------------------------------------------------------------
-template <typename T, int KB, int NST>
+// KT: D is not a multiple of NST stages of K, so the stages at the end of a row need the
+// per-lane K mask (the common shapes compile without it).
+template <typename T, int KB, int NST, bool KT>
 __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E,
                                                          const T* __restrict__ C, int N, int V,
                                                          int D, int n_split, int n_vt,
@@ -80,20 +82,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
   Acc acc;
   zero_acc(acc);
 
-  const int64_t ldb = (int64_t)D * sizeof(T);
+  const int ldb = D * (int)sizeof(T);
   uint32_t off[I];  // C and E tiles share the row length, hence the offsets
   kmajor_offsets<KB>(off, ldb, wave, lane);
+  // Classifier tile of the stages being issued: the current vocabulary tile (stages
+  // [t_first, t_first + n_k) of the stream) or, for the look-ahead, the next one.
+  int t_first = 0, v_cur = vt0 * kTile;
+  const T* c_cur = C + (int64_t)v_cur * D;
   auto issue = [&](int it) {
-    const int vt = vt0 + it / n_k, k0 = (it % n_k) * KS;
-    const int kc = (D - k0) / Traits<T>::kEpc;  // <= 0 on padding stages: all zeros
-    const int64_t kb = (int64_t)k0 * sizeof(T);
-    const T* oa = C + (int64_t)vt * kTile * D + k0;
-    const T* ob = E + (int64_t)tok0 * D + k0;
-    const int ra = tile_records(V, (int64_t)vt * kTile, ldb, kb);
-    const int rb = tile_records(N, tok0, ldb, kb);
+    const bool live = it < iters;   // past the end of the stream: zeros
+    const bool nx = it >= t_first + n_k;
+    const int k0 = (it - t_first - (nx ? n_k : 0)) * KS;
+    // valid K chunks from k0 (<= 0 on padding stages: all zeros)
+    const int kc = KT ? (D - k0) / Traits<T>::kEpc : Geo<KB>::kChunks;
+    const uint32_t soff = (uint32_t)k0 * sizeof(T);
+    const __amdgpu_buffer_rsrc_t rsC = kmajor_rsrc(c_cur + (nx ? (int64_t)kTile * D : 0),
+                                                   live ? V - v_cur - (nx ? kTile : 0) : 0, ldb);
+    const __amdgpu_buffer_rsrc_t rsE =
+        kmajor_rsrc(E + (int64_t)tok0 * D, live ? N - tok0 : 0, ldb);
     return stage_issue<KB>(
-        [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(oa, off, ra, kc, l, wave, lane, q0, q1); },
-        [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(ob, off, rb, kc, l, wave, lane, q0, q1); });
+        [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(rsC, off, soff, kc, l, wave, lane, q0, q1); },
+        [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(rsE, off, soff, kc, l, wave, lane, q0, q1); });
   };
   // Online log-sum-exp update for the finished tile, one token column group (ni) at a time.
   // Single pass against the running maximum m: t = z log2(e) - m, s += sum 2^t, with eight
@@ -101,26 +110,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
   // rebased to the new maximum.  If some value exceeds the running maximum by more than 2^64
   // (always on the first tile, where m = -inf), the wave recomputes the group exactly.
   auto epilogue = [&](int vt) {
-    const int vbase = vt * kTile + kWaveM * wm;
-    const bool full = vt * kTile + kTile <= V;
+    if (vt * kTile + kTile > V) {
+      // last vocabulary tile: rows at or past V take no part (-inf)
+      const int lim = V - vt * kTile - kWaveM * wm - acc_row_l(lane);
+#pragma unroll
+      for (int ni = 0; ni < kNB; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < kMB; ++mi)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (acc_row_c(mi, r) >= lim) acc[mi][ni][r] = -INFINITY;
+    }
 #pragma unroll
     for (int ni = 0; ni < kNB; ++ni) {
-      float x[64];
-#pragma unroll
-      for (int mi = 0; mi < kMB; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float z = acc[mi][ni][r];
-          x[16 * mi + r] = (full || vbase + 32 * mi + acc_row(r, lane) < V) ? z : -INFINITY;
-          acc[mi][ni][r] = 0.f;
-        }
       const float m = m_run[ni];
       float ps[8], pm[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) { ps[k] = 0.f; pm[k] = -INFINITY; }
 #pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const float t = __builtin_fmaf(x[i], kLog2e, -m);
+      for (int i = 0; i < 16 * kMB; ++i) {
+        const float t = __builtin_fmaf(acc[i >> 4][ni][i & 15], kLog2e, -m);
         ps[i & 7] += exp2_fast(t);
         pm[i & 7] = fmaxf(pm[i & 7], t);
       }
@@ -131,13 +140,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
         // exact update (rare): new maximum first, then the sum against it
         float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 64; ++i) mx = fmaxf(mx, x[i]);
+        for (int i = 0; i < 16 * kMB; ++i) mx = fmaxf(mx, acc[i >> 4][ni][i & 15]);
         const float m_new = fmaxf(m, mx * kLog2e);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
 #pragma unroll
         for (int k = 0; k < 8; ++k) ps[k] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 64; ++i) ps[i & 7] += exp2_fast(__builtin_fmaf(x[i], kLog2e, -m_use));
+        for (int i = 0; i < 16 * kMB; ++i)
+          ps[i & 7] += exp2_fast(__builtin_fmaf(acc[i >> 4][ni][i & 15], kLog2e, -m_use));
         const float tile = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
         s_run[ni] = s_run[ni] * exp2_fast(m - m_use) + tile;
         m_run[ni] = m_new;
@@ -147,6 +157,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
         s_run[ni] = (s_run[ni] + tile) * exp2_fast(-up);
         m_run[ni] = m + up;
       }
+#pragma unroll
+      for (int i = 0; i < 16 * kMB; ++i) acc[i >> 4][ni][i & 15] = 0.f;
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -154,6 +166,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
   const int n_tiles = vt1 - vt0;
   run_prologue<KB, NST>(iters, issue, B);
   for (int t = 0; t < n_tiles; ++t) {
+    t_first = t * n_k;
+    v_cur = (vt0 + t) * kTile;
+    c_cur = C + (int64_t)v_cur * D;
     run_stream<T, KB, NST, true, true>(t * n_k, n_k, iters, issue, B, acc, wm, wn, lane);
     epilogue(vt0 + t);
   }
@@ -273,7 +288,7 @@ struct BwdArgs {
   int accumulate;             // dE += (later chunks) instead of dE = (first chunk)
 };
 
-template <typename T, int KB, int NST>
+template <typename T, int KB, int NST, bool KT>
 __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const Bufs<NST>& B) {
   const T* __restrict__ E = A.E;
   const T* __restrict__ C = A.C;
@@ -303,20 +318,19 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
 
   Acc acc;
   zero_acc(acc);
-  const int64_t ldb = (int64_t)D * sizeof(T);
+  const int ldb = D * (int)sizeof(T);
   uint32_t off[I];
   kmajor_offsets<KB>(off, ldb, wave, lane);
   auto issue = [&](int it) {
+    const bool live = it < n_k;   // past the end of the stream: zeros
+    const __amdgpu_buffer_rsrc_t rsC = kmajor_rsrc(Cc + (int64_t)vl0 * D, live ? vc - vl0 : 0, ldb);
+    const __amdgpu_buffer_rsrc_t rsE = kmajor_rsrc(E + (int64_t)tok0 * D, live ? N - tok0 : 0, ldb);
     const int k0 = it * KS;
-    const int kc = (D - k0) / Traits<T>::kEpc;
-    const int64_t kb = (int64_t)k0 * sizeof(T);
-    const T* oa = Cc + (int64_t)vl0 * D + k0;
-    const T* ob = E + (int64_t)tok0 * D + k0;
-    const int ra = tile_records(vc, vl0, ldb, kb);
-    const int rb = tile_records(N, tok0, ldb, kb);
+    const int kc = KT ? (D - k0) / Traits<T>::kEpc : Geo<KB>::kChunks;
+    const uint32_t soff = (uint32_t)k0 * sizeof(T);
     return stage_issue<KB>(
-        [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(oa, off, ra, kc, l, wave, lane, q0, q1); },
-        [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(ob, off, rb, kc, l, wave, lane, q0, q1); });
+        [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(rsC, off, soff, kc, l, wave, lane, q0, q1); },
+        [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(rsE, off, soff, kc, l, wave, lane, q0, q1); });
   };
   // per column (token) constants, loaded before the main loop so their latency is hidden
   float coef[kNB], lse2[kNB];
@@ -354,17 +368,32 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int ni = 0; ni < kNB; ++ni) pmax[a][ni] = 0.f;
+  if (!full) {
+    // last tile of the chunk: rows at or past vc get p = 0
+    const int lim = vc - vl0 - kWaveM * wm - acc_row_l(lane);
+#pragma unroll
+    for (int ni = 0; ni < kNB; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < kMB; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (acc_row_c(mi, r) >= lim) acc[mi][ni][r] = -INFINITY;
+  }
+  // rows (within the wave's 128) are acc_row_c(mi, r) + acc_row_l(lane): compare the constant
+  // part with a per-lane value
+  int tcmp[kNB];
+#pragma unroll
+  for (int ni = 0; ni < kNB; ++ni) tcmp[ni] = trow[ni] - acc_row_l(lane);
 #pragma unroll
   for (int ni = 0; ni < kNB; ++ni)
 #pragma unroll
     for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = 32 * mi + acc_row(r, lane);  // row within this wave's 128 rows
-        float p = exp2_fast(__builtin_fmaf(acc[mi][ni][r], kLog2e, -lse2[ni]));
-        if (!full && vl0 + kWaveM * wm + row >= vc) p = 0.f;
+        const float p = exp2_fast(__builtin_fmaf(acc[mi][ni][r], kLog2e, -lse2[ni]));
         pmax[mi >> 1][ni] = fmaxf(pmax[mi >> 1][ni], p);
-        acc[mi][ni][r] = __builtin_fmaf(coef[ni], p, row == trow[ni] ? -coef[ni] : 0.f);
+        acc[mi][ni][r] =
+            __builtin_fmaf(coef[ni], p, acc_row_c(mi, r) == tcmp[ni] ? -coef[ni] : 0.f);
       }
   // the wave's 64 token columns are one filter block wide; its 128 vocabulary rows two blocks
   bool sig[2];
@@ -542,23 +571,26 @@ __device__ __forceinline__ void tile_bwd_de(const BwdArgs<T>& A, int lin, const 
   Acc acc;
   zero_acc(acc);
   if (n_act == 0 && accumulate) return;
-  const int64_t ldb = (int64_t)D * sizeof(T);
+  const int ldb = D * (int)sizeof(T);
   uint32_t offA[I], offB[I];
-  kmajor_offsets<KB>(offA, ldg * (int64_t)sizeof(T), wave, lane);
+  kmajor_offsets<KB>(offA, (int)ldg * (int)sizeof(T), wave, lane);
   mn_offsets<T, KB>(offB, ldb, d0, D, wave, lane);
+  const T* gt = G + (int64_t)tok0 * ldg;
+  const int g_rec = kTile * (int)ldg * (int)sizeof(T);
   auto issue = [&](int i) {
-    const int e = __builtin_amdgcn_readfirstlane(sList[i]);
+    const bool live = i < n_act;   // past the end of the list: zeros
+    const int e = __builtin_amdgcn_readfirstlane(sList[live ? i : 0]);
     const int k0 = (e >> 4) * KS;
     const bool zero = (e >> (wave >> 1)) & 1;  // wave w loads token rows 32 w .. 32 w + 31
-    const T* oa = G + (int64_t)tok0 * ldg + k0;
-    const T* ob = Cc + (int64_t)k0 * D + d0;
-    const int ra = zero ? 0 : kRecords;
-    const int rb = tile_records(vc, k0, ldb, (int64_t)d0 * sizeof(T));
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(gt, (zero || !live) ? 0 : g_rec);
+    const __amdgpu_buffer_rsrc_t rb = mn_rsrc<T, KB>(Cc + (int64_t)k0 * D + d0,
+                                                     live ? vc - k0 : 0, ldb, d0 * (int)sizeof(T));
+    const uint32_t soff = (uint32_t)k0 * sizeof(T);
     return stage_issue<KB>(
         [=, &offA](char* l, int q0, int q1) {
-          kmajor_issue<KB>(oa, offA, ra, Geo<KB>::kChunks, l, wave, lane, q0, q1);
+          kmajor_issue<KB>(ra, offA, soff, Geo<KB>::kChunks, l, wave, lane, q0, q1);
         },
-        [=, &offB](char* l, int q0, int q1) { mn_issue<T, KB>(ob, offB, rb, 0u, l, wave, lane, q0, q1); });
+        [=, &offB](char* l, int q0, int q1) { mn_issue<T, KB>(rb, offB, 0u, l, wave, lane, q0, q1); });
   };
   if (n_act > 0) {
     run_prologue<KB, NST>(n_act, issue, B);
@@ -593,9 +625,10 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
   const int wm = wave_m(wave), wn = wave_n(wave);
   const int vl0 = vt * kTile, d0 = dt * kTile;
   const int n_stages = n_pad / KS;
-  const int64_t ldb = (int64_t)D * sizeof(T);
+  const int ldb = D * (int)sizeof(T);
+  const int ldgb = (int)ldg * (int)sizeof(T);
   uint32_t offA[I], offB[I];
-  mn_offsets<T, KB>(offA, ldg * (int64_t)sizeof(T), vl0, (int)ldg, wave, lane);
+  mn_offsets<T, KB>(offA, ldgb, vl0, (int)ldg, wave, lane);
   mn_offsets<T, KB>(offB, ldb, d0, D, wave, lane);
   Acc acc;
   zero_acc(acc);
@@ -604,17 +637,17 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
     const int n_act = build_stage_list<KS, NST>(flags + (int64_t)((sbase * KS) >> 6) * fstride,
                                                 fstride, cnt, false, vt * 4, sList, sCnt);
     auto issue = [&](int i) {
-      const int e = __builtin_amdgcn_readfirstlane(sList[i]);
+      const bool live = i < n_act;   // past the end of the list: zeros
+      const int e = __builtin_amdgcn_readfirstlane(sList[live ? i : 0]);
       const int k0 = (sbase + (e >> 4)) * KS;
-      const T* oa = G + (int64_t)k0 * ldg + vl0;
-      const T* ob = E + (int64_t)k0 * D + d0;
       const uint32_t zc = (uint32_t)(e & 15);
-      const int rb = tile_records(N, k0, ldb, (int64_t)d0 * sizeof(T));
+      const __amdgpu_buffer_rsrc_t ra = mn_rsrc<T, KB>(
+          G + (int64_t)k0 * ldg + vl0, live ? n_pad - k0 : 0, ldgb, vl0 * (int)sizeof(T));
+      const __amdgpu_buffer_rsrc_t rb = mn_rsrc<T, KB>(E + (int64_t)k0 * D + d0,
+                                                       live ? N - k0 : 0, ldb, d0 * (int)sizeof(T));
       return stage_issue<KB>(
-          [=, &offA](char* l, int q0, int q1) {
-            mn_issue<T, KB>(oa, offA, kRecords, zc, l, wave, lane, q0, q1);
-          },
-          [=, &offB](char* l, int q0, int q1) { mn_issue<T, KB>(ob, offB, rb, 0u, l, wave, lane, q0, q1); });
+          [=, &offA](char* l, int q0, int q1) { mn_issue<T, KB>(ra, offA, zc, l, wave, lane, q0, q1); },
+          [=, &offB](char* l, int q0, int q1) { mn_issue<T, KB>(rb, offB, 0u, l, wave, lane, q0, q1); });
     };
     if (n_act > 0) {
       run_prologue<KB, NST>(n_act, issue, B);
@@ -631,10 +664,10 @@ __host__ __device__ inline int bwd_items(int rows, int cols) {
 }
 
 // Backward step 1 alone (the first chunk): one G tile per workgroup.
-template <typename T, int KB, int NST>
+template <typename T, int KB, int NST, bool KT>
 __global__ __launch_bounds__(kThreads, 1) void k_bwd_g(BwdArgs<T> A) {
   CCE_STAGE_BUFFERS(KB, NST, B)
-  tile_bwd_g<T, KB, NST>(A, xcd_remap(blockIdx.x, gridDim.x), B);
+  tile_bwd_g<T, KB, NST, KT>(A, xcd_remap(blockIdx.x, gridDim.x), B);
 }
 
 // Backward steps 2 and 3 of chunk c (dE and dC tiles, the long ones) fused with step 1 of
@@ -642,7 +675,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_g(BwdArgs<T> A) {
 // short tiles fill the CUs that the 2 x (N/256) x (D/256) long tiles leave idle.  Workgroups
 // [0, r_de) compute dE tiles, [r_de, r_de + r_dc) dC tiles, the rest G tiles of `next`
 // (none when n_next_items == 0).  Each range is a multiple of 8 and renumbered per XCD.
-template <typename T, int KB, int NST>
+template <typename T, int KB, int NST, bool KT>
 __global__ __launch_bounds__(kThreads, 1) void k_bwd_fused(BwdArgs<T> A, BwdArgs<T> next,
                                                            int r_de, int r_dc) {
   CCE_STAGE_BUFFERS(KB, NST, B)
@@ -655,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_fused(BwdArgs<T> A, BwdArgs
     tile_bwd_dc<T, KB, NST>(A, xcd_remap(b - r_de, r_dc), B, sList, sCnt);
   } else {
     const int n = (int)gridDim.x - r_de - r_dc;
-    tile_bwd_g<T, KB, NST>(next, xcd_remap(b - r_de - r_dc, n), B);
+    tile_bwd_g<T, KB, NST, KT>(next, xcd_remap(b - r_de - r_dc, n), B);
   }
 }
 

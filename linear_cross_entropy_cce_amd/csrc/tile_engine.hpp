@@ -71,20 +71,28 @@ __device__ __forceinline__ void wait_vmcnt() {
 // ---------------------------------------------------------------------------------------
 // HBM -> LDS stage loads with buffer_load ... lds.  One instruction moves 64 lanes x 16 bytes
 // into 1 KB of consecutive LDS.  Every lane keeps a fixed byte offset per instruction relative
-// to the stage's tile origin (a uniform pointer turned into a buffer descriptor); masked lanes
-// use an offset past the descriptor's range, which the hardware answers with zeros.  The XOR
+// to a tile origin (a uniform pointer turned into a buffer descriptor); masked lanes use an
+// offset past the descriptor's range, which the hardware answers with zeros.  The XOR
 // swizzles make the fragment reads below free of bank conflicts: a lane picks which global
 // chunk lands in its fixed LDS slot.
 // ---------------------------------------------------------------------------------------
 constexpr uint32_t kOob = 0x80000000u;         // offset answered with zeros
 constexpr int kRecords = 0x7FFFFFF0;           // descriptor range
 
+// Base and range are workgroup-uniform; readfirstlane states it, so the descriptor always
+// lives in scalar registers (never a per-lane "waterfall" loop over the loads).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int records) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, records, 0x00020000);
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  void* const pu = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, __builtin_amdgcn_readfirstlane(records),
+                                           0x00020000);
 }
 
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
+                                           uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
 }
 
 // Stage geometry.  KB = bytes of K per K-major operand row per stage (128 or 64): one
@@ -125,29 +133,30 @@ __device__ __forceinline__ void kmajor_offsets(uint32_t (&off)[Geo<KB>::kIssue],
   }
 }
 
-// Valid bytes from a tile origin at (row0, k0) of a row-major operand with row_lim rows:
-// every chunk of a row < row_lim lies below it and every chunk of a later row above it.
-__device__ __forceinline__ int tile_records(int64_t row_lim, int64_t row0, int64_t ld_bytes,
-                                            int64_t k0_bytes) {
-  const int64_t b = (row_lim - row0) * ld_bytes - k0_bytes;
-  return b <= 0 ? 0 : (b > kRecords ? kRecords : (int)b);
+// Descriptor of a K-major operand tile whose first row (at K = 0) is `origin`, with rows_left
+// rows of the operand from there: its range ends with the tile's last valid row, so later
+// rows load as zeros.  Stages step through K with the scalar offset of the loads, which
+// leaves the row test unchanged (a chunk never reaches past its own row).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t kmajor_rsrc(const void* origin, int rows_left,
+                                                              int ld_bytes) {
+  const int rows = rows_left < 0 ? 0 : (rows_left > kTile ? kTile : rows_left);
+  return make_rsrc(origin, rows * ld_bytes);
 }
 
-// Instructions [q0, q1) of this wave's share of a stage.  k_chunks = valid 16-byte K chunks
-// left from k0 (>= chunks per row: full stage).
+// Instructions [q0, q1) of this wave's share of a stage at byte offset soff along K.
+// k_chunks = valid 16-byte K chunks left from the stage's K origin (>= chunks per row: full).
 template <int KB>
-__device__ __forceinline__ void kmajor_issue(const void* origin,
-                                             const uint32_t (&off)[Geo<KB>::kIssue], int records,
-                                             int k_chunks, char* lds, int wave, int lane,
-                                             int q0 = 0, int q1 = Geo<KB>::kIssue) {
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(origin, records);
+__device__ __forceinline__ void kmajor_issue(__amdgpu_buffer_rsrc_t rs,
+                                             const uint32_t (&off)[Geo<KB>::kIssue],
+                                             uint32_t soff, int k_chunks, char* lds, int wave,
+                                             int lane, int q0 = 0, int q1 = Geo<KB>::kIssue) {
 #pragma unroll
   for (int q = 0; q < Geo<KB>::kIssue; ++q) {
     if (q < q0 || q >= q1) continue;
     uint32_t o = off[q];
     if (k_chunks < Geo<KB>::kChunks)
       o = kmajor_chunk<KB>(kmajor_row<KB>(wave, q, lane), lane) < k_chunks ? o : kOob;
-    lds_load16(rs, lds + (wave * Geo<KB>::kIssue + q) * 1024, o);
+    lds_load16(rs, lds + (wave * Geo<KB>::kIssue + q) * 1024, o, soff);
   }
 }
 
@@ -178,18 +187,30 @@ __device__ __forceinline__ void mn_offsets(uint32_t (&off)[Geo<KB>::kIssue], int
   }
 }
 
+// Descriptor of one MN-major stage whose origin (row k0, column col0) is `origin`, with
+// rows_left rows of the operand from k0 and col0 at byte col0_bytes of its row: the range ends
+// with the stage's last valid row.
+template <typename T, int KB>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mn_rsrc(const void* origin, int rows_left,
+                                                          int ld_bytes, int col0_bytes) {
+  constexpr int R = KB / (int)sizeof(T);
+  const int rows = rows_left < 0 ? 0 : (rows_left > R ? R : rows_left);
+  const int rec = rows * ld_bytes - col0_bytes;
+  return make_rsrc(origin, rec < 0 ? 0 : rec);
+}
+
 // Instructions [q0, q1).  zero_cols bit b = load zeros for columns 64 b .. 64 b + 63.
 template <typename T, int KB>
-__device__ __forceinline__ void mn_issue(const void* origin, const uint32_t (&off)[Geo<KB>::kIssue],
-                                         int records, uint32_t zero_cols, char* lds, int wave,
-                                         int lane, int q0 = 0, int q1 = Geo<KB>::kIssue) {
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(origin, records);
+__device__ __forceinline__ void mn_issue(__amdgpu_buffer_rsrc_t rs,
+                                         const uint32_t (&off)[Geo<KB>::kIssue],
+                                         uint32_t zero_cols, char* lds, int wave, int lane,
+                                         int q0 = 0, int q1 = Geo<KB>::kIssue) {
 #pragma unroll
   for (int q = 0; q < Geo<KB>::kIssue; ++q) {
     if (q < q0 || q >= q1) continue;
     uint32_t o = off[q];
     if (zero_cols) o = ((zero_cols >> (mn_col<T, KB>(wave, q, lane) >> 6)) & 1u) ? kOob : o;
-    lds_load16(rs, lds + (wave * Geo<KB>::kIssue + q) * 1024, o);
+    lds_load16(rs, lds + (wave * Geo<KB>::kIssue + q) * 1024, o, 0u);
   }
 }
 
@@ -283,6 +304,12 @@ struct NoIssue {
   __device__ __forceinline__ void one(int) const {}
 };
 
+// Pins an accumulator in the instruction order.  MFMA builtins have no side effects, so the
+// code generator may move them across loads and barriers; an (empty) volatile asm statement
+// that reads and writes the accumulator cannot move relative to other side effects, and the
+// MFMAs that produce or consume the accumulator stay on their side of it.
+__device__ __forceinline__ void pin(f32x16_t& acc) { asm volatile("" : "+v"(acc)); }
+
 // One stage of MFMAs for this wave: KB / 32 k-groups x 4 x 2 blocks.  While the 8 MFMAs of the
 // first k-group run, part.one(j) issues the j-th load of a later stage, one after each MFMA,
 // so the address units never stall the MFMA issue and the loads get the rest of the stage to
@@ -321,14 +348,24 @@ __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Ac
     for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
       for (int ni = 0; ni < kNB; ++ni) {
-        mma(acc[mi][ni], a[c][mi], b[c][ni]);
         if (g == 0) {
+          // MFMA j, then load j: the pins keep MFMA j after load j - 1 and before load j
+          pin(acc[mi][ni]);
+          mma(acc[mi][ni], a[c][mi], b[c][ni]);
+          pin(acc[mi][ni]);
           part.one(kNB * mi + ni);
           __builtin_amdgcn_sched_barrier(0);
+        } else {
+          mma(acc[mi][ni], a[c][mi], b[c][ni]);
         }
       }
     __builtin_amdgcn_sched_barrier(0);
   }
+  // every MFMA of the stage before whatever follows (the next stage's wait and barrier)
+#pragma unroll
+  for (int mi = 0; mi < kMB; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNB; ++ni) pin(acc[mi][ni]);
 }
 
 // Workgroup barrier between pipeline stages.  Each wave has already waited (vmcnt) for its
@@ -363,40 +400,51 @@ __device__ __forceinline__ void wait_stages(int keep) {
   }
 }
 
+// Loads of one later stage, spread over the MFMAs of the current one (compute_stage).
+template <int KB, typename St>
+struct StagePart {
+  const St& st;
+  char* na;
+  char* nb;
+  __device__ __forceinline__ void one(int j) const {
+    if (j < 2 * Geo<KB>::kIssue) st.one(na, nb, j);
+  }
+};
+
+// One round of NST stages g0 .. g0 + NST - 1 (stage g0 + u in buffer u).  Every stage issues
+// the loads of stage g + P (P = NST - 1) into the buffer freed by stage g - 1; past the end of
+// the stream issue() hands out empty descriptors, so those loads only fill zeros.  (A branch
+// around them would split the MFMA sequence, and a separate copy of the last round costs
+// the register allocator a second live copy of the accumulators.)
+template <typename T, int KB, int NST, bool AK, bool BK, typename Issue>
+__device__ __forceinline__ void run_round(int g0, Issue& issue, const Bufs<NST>& B, Acc& acc,
+                                          int wm, int wn, int lane) {
+  constexpr int P = NST - 1;   // prefetch distance
+#pragma unroll
+  for (int u = 0; u < NST; ++u) {
+    // stage g0 + u has landed once at most P - 1 later stages are still in flight
+    wait_stages<KB, NST>(P - 1);
+    stage_barrier();
+    const auto st = issue(g0 + u + P);   // per-stage address setup, once
+    const StagePart<KB, decltype(st)> part{st, B.a[(u + P) % NST], B.b[(u + P) % NST]};
+    compute_stage<T, KB, AK, BK>(B.a[u], B.b[u], acc, wm, wn, lane, part);
+  }
+}
+
 // Software pipeline over stages [base, base + n) of a stream of `total` stages; base and n
 // are multiples of NST, so stage g lives in buffer g % NST.  Stages base .. base + NST - 2
 // must already be issued (run_prologue); while stage g is computed, the loads of stages
 // g + 1 .. g + NST - 1 are in flight.  Issuing continues into the next tile of the stream.
-// issue(g) prepares stage g and returns a StageIssue for it.
+// issue(g) prepares stage g (for g >= total: loads of zeros) and returns a StageIssue for it.
+// At the end of the stream the zero loads are waited for, so no load into LDS is left in
+// flight.
 template <typename T, int KB, int NST, bool AK, bool BK, typename Issue>
 __device__ __forceinline__ void run_stream(int base, int n, int total, Issue&& issue,
                                            const Bufs<NST>& B, Acc& acc, int wm, int wn,
                                            int lane) {
-  constexpr int P = NST - 1;   // prefetch distance
-  for (int j = 0; j < n; j += NST) {
-#pragma unroll
-    for (int u = 0; u < NST; ++u) {
-      const int g = base + j + u;
-      // stages issued after g: g + 1 .. min(g + P - 1, total - 1)
-      const int ahead = min(P - 1, total - 1 - g);
-      wait_stages<KB, NST>(ahead);
-      stage_barrier();
-      const bool more = g + P < total;
-      char* const na = B.a[(u + P) % NST];
-      char* const nb = B.b[(u + P) % NST];
-      const auto st = issue(more ? g + P : g);   // per-stage address setup, once
-      struct Part {
-        const decltype(st)& st;
-        bool more;
-        char* na;
-        char* nb;
-        __device__ __forceinline__ void one(int j) const {
-          if (more && j < 2 * Geo<KB>::kIssue) st.one(na, nb, j);
-        }
-      } part{st, more, na, nb};
-      compute_stage<T, KB, AK, BK>(B.a[u], B.b[u], acc, wm, wn, lane, part);
-    }
-  }
+  for (int g0 = base; g0 < base + n; g0 += NST)
+    run_round<T, KB, NST, AK, BK>(g0, issue, B, acc, wm, wn, lane);
+  if (base + n >= total) wait_vmcnt<0>();
 }
 
 // Issues the first NST - 1 stages of a stream (fewer if the stream is shorter).
@@ -423,6 +471,14 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
 __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
+// The same split into a compile-time part (block mi of the wave's rows, register r) and a
+// per-lane part: row within the wave's 128 rows = acc_row_c(mi, r) + acc_row_l(lane).  Tests
+// against a row bound then compare a constant with one per-lane value, instead of keeping
+// 64 row indices per lane alive.
+__host__ __device__ constexpr int acc_row_c(int mi, int r) {
+  return 32 * mi + 8 * (r >> 2) + (r & 3);
+}
+__device__ __forceinline__ int acc_row_l(int lane) { return 4 * (lane >> 5); }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8).
 // Renumber so that each XCD receives a contiguous range of logical work items, which then
