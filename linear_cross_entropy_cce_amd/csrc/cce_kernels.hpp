@@ -308,7 +308,7 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
   constexpr int I = Geo<KB>::kIssue;
 
   int tb, vt;
-  grouped_tile(lin, n_vtc, tb, vt);
+  grouped_tile(lin, n_tb, n_vtc, tb, vt);
   if (tb >= n_tb || vt >= n_vtc) return;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave_m(wave), wn = wave_n(wave);
@@ -534,7 +534,8 @@ __device__ __forceinline__ int build_stage_list(const uint8_t* __restrict__ flag
   // whole rounds of stages
   const int padded = (total + NST - 1) / NST * NST;
   if (padded != total) {
-    if ((int)threadIdx.x < padded - total) list[total + threadIdx.x] = 15;
+    if (threadIdx.x == 0)
+      for (int i = total; i < padded; ++i) list[i] = 15;
     __syncthreads();
   }
   return padded;
@@ -559,7 +560,7 @@ __device__ __forceinline__ void tile_bwd_de(const BwdArgs<T>& A, int lin, const 
   float* __restrict__ dE = A.dE;
   const int accumulate = A.accumulate;
   int tb, dt;
-  grouped_tile(lin, n_dt, tb, dt);
+  grouped_tile(lin, n_tb, n_dt, tb, dt);
   if (tb >= n_tb || dt >= n_dt) return;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave_m(wave), wn = wave_n(wave);
@@ -619,7 +620,7 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
   const int fstride = A.fstride;
   float* __restrict__ dCc = A.dC + (int64_t)A.v0 * A.D;
   int vt, dt;
-  grouped_tile(lin, n_dt, vt, dt);
+  grouped_tile(lin, n_vtc, n_dt, vt, dt);
   if (vt >= n_vtc || dt >= n_dt) return;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave_m(wave), wn = wave_n(wave);
@@ -658,10 +659,8 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
   store_tile(dCc, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc, lane, false);
 }
 
-// Work items of the backward launches, in super-blocks of 4 x 8 tiles.
-__host__ __device__ inline int bwd_items(int rows, int cols) {
-  return ((rows + 3) / 4) * ((cols + 7) / 8) * 32;
-}
+// Work items of the backward launches: one per tile (grouped_tile).
+__host__ __device__ inline int bwd_items(int rows, int cols) { return rows * cols; }
 
 // Backward step 1 alone (the first chunk): one G tile per workgroup.
 template <typename T, int KB, int NST, bool KT>

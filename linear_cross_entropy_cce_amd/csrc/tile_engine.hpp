@@ -487,13 +487,21 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid & 7) * (nblocks >> 3) + (bid >> 3);
 }
 
-// Logical item -> (row tile, column tile) in super-blocks of 4 x 8 tiles, so the 32
-// workgroups an XCD runs at once read 4 + 8 distinct operand tiles.
-__device__ __forceinline__ void grouped_tile(int lin, int cols, int& r, int& c) {
-  const int sb_cols = (cols + 7) >> 3;
-  const int sb = lin >> 5, w = lin & 31;
-  r = (sb / sb_cols) * 4 + (w >> 3);
-  c = (sb % sb_cols) * 8 + (w & 7);
+// Logical item -> (row tile, column tile) of a rows x cols tile grid, in super-blocks of up to
+// 4 x 8 tiles (narrower or shorter at the right and bottom edges), so the 32 workgroups an XCD
+// runs at once read about 4 + 8 distinct operand tiles.  Items are numbered row group by row
+// group and, within one, column group by column group; exactly rows x cols items are valid
+// (lin >= rows x cols gives r >= rows).
+__device__ __forceinline__ void grouped_tile(int lin, int rows, int cols, int& r, int& c) {
+  const int rg = lin / (4 * cols);
+  const int hr = min(4, rows - 4 * rg);
+  if (hr <= 0) { r = rows; c = 0; return; }
+  int w = lin - rg * 4 * cols;
+  const int cg = w / (hr * 8);
+  const int wc = min(8, cols - 8 * cg);
+  w -= cg * hr * 8;
+  r = 4 * rg + w / wc;
+  c = 8 * cg + w % wc;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
