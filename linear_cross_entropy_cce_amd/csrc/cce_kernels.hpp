@@ -453,7 +453,9 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
 
 // Writes (or adds) this wave's 128 x 64 accumulators to a row-major fp32 matrix out[rows][ld]
 // at (row0, col0); rows >= row_lim and columns >= col_lim are dropped.  For each register a
-// half-wave writes 32 consecutive columns (128 bytes).
+// half-wave writes 32 consecutive columns (128 bytes).  Adding uses the L2's float atomic add
+// without return, so no load latency is exposed; it stays deterministic because each element
+// receives one add per launch and launches are ordered on the stream.
 __device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, int row0,
                                            int row_lim, int col0, int col_lim, Acc& acc,
                                            int lane, bool add) {
@@ -476,7 +478,7 @@ __device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, 
         for (int r = 0; r < 16; ++r) {
           float* p =
               out + (int64_t)(row0 + 32 * mi + acc_row(r, lane)) * ld + col0 + 32 * ni + (lane & 31);
-          *p += acc[mi][ni][r];
+          atomicAddNoRet(p, acc[mi][ni][r]);
         }
   } else {
 #pragma unroll
@@ -488,7 +490,10 @@ __device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, 
           const int row = row0 + 32 * mi + acc_row(r, lane), col = col0 + 32 * ni + (lane & 31);
           if (row < row_lim && col < col_lim) {
             float* p = out + (int64_t)row * ld + col;
-            *p = add ? *p + acc[mi][ni][r] : acc[mi][ni][r];
+            if (add)
+              atomicAddNoRet(p, acc[mi][ni][r]);
+            else
+              *p = acc[mi][ni][r];
           }
         }
   }
