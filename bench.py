@@ -73,6 +73,75 @@ def cpu_baseline(d, w, n_tokens: int) -> dict:
                       f"contribution over all V={w.V}), {dt:.1f} s"}
 
 
+def vendor_gemm_reference(dev) -> dict:
+    """Context for the MFMA roofline: the vendor library GEMM (torch.mm, hipBLASLt on ROCm) on
+    random bf16 operands of the forward's shape class, timed on the same GPU in the same run.
+    Dense bf16 MFMA throughput with random data is bounded by the board's power limit well
+    below the published peak; this number shows where that bound sits right now."""
+    import torch
+    M, Nn, K = 8192, 32768, 2304
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    a = torch.randn(M, K, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(K, Nn, device=dev, dtype=torch.bfloat16, generator=g)
+    c = torch.empty(M, Nn, device=dev, dtype=torch.bfloat16)
+    for _ in range(5):
+        torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    iters = 20
+    s.record()
+    for _ in range(iters):
+        torch.mm(a, b, out=c)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / iters
+    return {"op": f"torch.mm bf16 randn {M}x{K} @ {K}x{Nn}", "tflops": 2.0 * M * Nn * K / (ms * 1e-3) / 1e12}
+
+
+def sample_clock(step, seconds: float = 2.5) -> dict | None:
+    """GFX clock and board power while the step runs back to back (outside the timed region):
+    amd-smi is polled from a thread; its readings refresh about once a second."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    if shutil.which("amd-smi") is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c"], capture_output=True,
+                                   text=True, timeout=10).stdout
+            except Exception:  # pragma: no cover
+                return
+            p = re.search(r"SOCKET_POWER:\s*(\d+)", r)
+            clk = [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)", r)]
+            if p and clk:
+                samples.append((float(p.group(1)), sum(clk) / len(clk)))
+            stop.wait(0.2)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    busy = samples[1:] if len(samples) > 2 else samples   # first reading may predate the load
+    if not busy:
+        return None
+    mhz = sum(c for _, c in busy) / len(busy)
+    return {"gfx_mhz_mean": mhz, "socket_power_w_mean": sum(p for p, _ in busy) / len(busy),
+            "samples": len(busy), "how": f"amd-smi polled while the step ran {seconds} s back to back",
+            "bf16_dense_peak_at_this_clock_tflops": 256 * 4096 * mhz * 1e6 / 1e12}
+
+
 def copy_calibration() -> int:
     import torch
     n = 1 << 30
@@ -96,6 +165,10 @@ def main() -> int:
                     help="override the workload's gradient filter threshold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the GPU clock / power sampling after the timed region")
+    ap.add_argument("--no-gemm-ref", action="store_true",
+                    help="skip the vendor-GEMM reference measurement (context only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times): the reference kernel "
                          "for scaling the HBM byte counters of a profiler")
@@ -155,16 +228,18 @@ def main() -> int:
     torch.cuda.synchronize()
     peak_extra = torch.cuda.max_memory_allocated() - base_alloc
 
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     cce.timing_begin(max_launches=args.steps * 200)
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         step()
-    stop.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     kernels = cce.timing_end()
-    ms = start.elapsed_time(stop) / args.steps
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    clock = None if args.no_clock else sample_clock(step)
 
     flop_fwd = 2.0 * N * V * D
     flop_bwd = 6.0 * N * V * D
@@ -197,6 +272,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": step_ms[len(step_ms) // 2],
+        "ms_per_step_min": step_ms[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -222,6 +299,10 @@ def main() -> int:
         "input_generation_s": gen_s,
         "kernel_source_hash": kernel_source_hash(),
     }
+    if clock is not None:
+        out["context"]["clock_during_run"] = clock
+    if not args.no_gemm_ref:
+        out["context"]["vendor_gemm_same_gpu"] = vendor_gemm_reference(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, w, args.cpu_tokens)
     print(json.dumps(out), flush=True)
