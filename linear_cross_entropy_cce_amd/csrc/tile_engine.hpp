@@ -315,34 +315,40 @@ __device__ __forceinline__ void pin(f32x16_t& acc) { asm volatile("" : "+v"(acc)
 // so the address units never stall the MFMA issue and the loads get the rest of the stage to
 // land.  K-major fragments of group g + 1 are read while group g runs.  Transposing LDS reads
 // carry no alias information for the compiler, which would make each of them wait for every
-// direct-to-LDS load in flight, so with an MN-major operand all fragments of the stage are
-// read before the loads are issued.  Scheduling barriers keep this order.
+// direct-to-LDS load in flight, so the fragments of an MN-major bf16 operand are all read, for
+// every group of the stage, before the loads are issued.  Scheduling barriers and the
+// accumulator pins keep this order.
 template <typename T, int KB, bool AK, bool BK, typename Part = NoIssue>
 __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Acc& acc, int wm,
                                               int wn, int lane, const Part& part = Part()) {
   typedef typename Traits<T>::frag_t F;
   constexpr int G = Geo<KB>::kGroups;
-  constexpr bool kEarly = sizeof(T) == 2 && (!AK || !BK);
-  constexpr int S = kEarly ? G : 2;
-  F a[S][kMB], b[S][kNB];
-  auto read = [&](int slot, int g) {
+  constexpr bool kEA = sizeof(T) == 2 && !AK;   // operand read for the whole stage up front
+  constexpr bool kEB = sizeof(T) == 2 && !BK;
+  constexpr int SA = kEA ? G : 2, SB = kEB ? G : 2;
+  F a[SA][kMB], b[SB][kNB];
+  auto read_a = [&](int slot, int g) {
 #pragma unroll
     for (int i = 0; i < kMB; ++i) a[slot][i] = frag<T, KB, AK>(As, kWaveM * wm + 32 * i, g, lane);
+  };
+  auto read_b = [&](int slot, int g) {
 #pragma unroll
     for (int i = 0; i < kNB; ++i) b[slot][i] = frag<T, KB, BK>(Bs, kWaveN * wn + 32 * i, g, lane);
   };
-  if constexpr (kEarly) {
+  read_a(0, 0);
+  read_b(0, 0);
 #pragma unroll
-    for (int g = 0; g < G; ++g) read(g, g);
-  } else {
-    read(0, 0);
+  for (int g = 1; g < G; ++g) {
+    if (kEA) read_a(g, g);
+    if (kEB) read_b(g, g);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int c = kEarly ? g : (g & 1);
-    if constexpr (!kEarly) {
-      if (g + 1 < G) read((g + 1) & 1, g + 1);
+    const int ca = kEA ? g : (g & 1), cb = kEB ? g : (g & 1);
+    if (g + 1 < G) {
+      if (!kEA) read_a((g + 1) & 1, g + 1);
+      if (!kEB) read_b((g + 1) & 1, g + 1);
     }
 #pragma unroll
     for (int mi = 0; mi < kMB; ++mi)
@@ -351,12 +357,12 @@ __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Ac
         if (g == 0) {
           // MFMA j, then load j: the pins keep MFMA j after load j - 1 and before load j
           pin(acc[mi][ni]);
-          mma(acc[mi][ni], a[c][mi], b[c][ni]);
+          mma(acc[mi][ni], a[ca][mi], b[cb][ni]);
           pin(acc[mi][ni]);
           part.one(kNB * mi + ni);
           __builtin_amdgcn_sched_barrier(0);
         } else {
-          mma(acc[mi][ni], a[c][mi], b[c][ni]);
+          mma(acc[mi][ni], a[ca][mi], b[cb][ni]);
         }
       }
     __builtin_amdgcn_sched_barrier(0);
