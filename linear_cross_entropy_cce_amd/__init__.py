@@ -8,7 +8,8 @@ from ._lib import (KERNEL_KINDS, CCEError, LIB_PATH, backward_chunk, backward_wo
                    cce_backward, cce_forward, cce_loss_mean, forward_splits,
                    forward_workspace_bytes, lib, loss_mean_workspace_bytes, timing_begin,
                    timing_end)
+from .autograd import LinearCrossEntropy, linear_cross_entropy
 
-__all__ = ["CCEError", "LIB_PATH", "backward_chunk", "backward_workspace_bytes", "cce_backward",
+__all__ = ["LinearCrossEntropy", "linear_cross_entropy", "CCEError", "LIB_PATH", "backward_chunk", "backward_workspace_bytes", "cce_backward",
            "cce_forward", "cce_loss_mean", "forward_splits", "forward_workspace_bytes", "lib",
            "loss_mean_workspace_bytes", "KERNEL_KINDS", "timing_begin", "timing_end"]

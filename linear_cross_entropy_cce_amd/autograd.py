@@ -1,0 +1,125 @@
+"""torch.autograd integration of libcce: the Cut Cross-Entropy loss as a differentiable op.
+
+    loss = linear_cross_entropy(E, C, targets, ignore_index=-100, filter_eps=2**-12,
+                                reduction="mean")
+
+E [N,D] (token embeddings) and C [V,D] (classifier rows) are CUDA tensors of one dtype (bf16 or
+fp32); targets [N] int64.  The loss of token n is lse_v(E_n . C_v) - E_n . C_t(n), 0 for ignored
+tokens (the Cut Cross-Entropy abstract, taxoreview.com page dblp:393/3562, sentences 4-6); the
+backward skips 64 x 64 blocks of the softmax gradient whose entries are all below filter_eps
+(sentence 9; 0 disables it).
+
+Every step of the computation runs in libcce's kernels (cce_forward / cce_backward /
+cce_loss_mean); this module only routes tensors and gradients:
+  * "none": per-token losses; the backward passes the upstream gradient as libcce's dloss;
+  * "sum":  the per-token losses summed (dloss = the upstream scalar for every token);
+  * "mean": libcce's mean call, which returns the mean over non-ignored tokens together with
+    its gradients in one pass; the backward scales them by the upstream scalar.
+Gradients come back in the dtype of E and C (libcce computes them in fp32).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+FILTER_EPS = 2.0 ** -12
+
+
+def _to_param_dtype(g: torch.Tensor, like: torch.Tensor) -> torch.Tensor:
+    return g if g.dtype == like.dtype else g.to(like.dtype)
+
+
+class _PerToken(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, E, C, targets, ignore_index, filter_eps):
+        loss, lse = _lib.cce_forward(E, C, targets, ignore_index)
+        ctx.save_for_backward(E, C, targets, lse)
+        ctx.ignore_index = ignore_index
+        ctx.filter_eps = filter_eps
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        E, C, targets, lse = ctx.saved_tensors
+        if not (ctx.needs_input_grad[0] or ctx.needs_input_grad[1]):
+            return None, None, None, None, None
+        dloss = grad_loss.to(torch.float32).contiguous()
+        dE, dC = _lib.cce_backward(dloss, E, C, targets, lse, ctx.ignore_index, ctx.filter_eps)
+        return (_to_param_dtype(dE, E) if ctx.needs_input_grad[0] else None,
+                _to_param_dtype(dC, C) if ctx.needs_input_grad[1] else None, None, None, None)
+
+
+class _Sum(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, E, C, targets, ignore_index, filter_eps):
+        loss, lse = _lib.cce_forward(E, C, targets, ignore_index)
+        ctx.save_for_backward(E, C, targets, lse)
+        ctx.ignore_index = ignore_index
+        ctx.filter_eps = filter_eps
+        return loss.sum()
+
+    @staticmethod
+    def backward(ctx, grad_sum):
+        E, C, targets, lse = ctx.saved_tensors
+        if not (ctx.needs_input_grad[0] or ctx.needs_input_grad[1]):
+            return None, None, None, None, None
+        dloss = grad_sum.to(torch.float32).reshape(1).contiguous()   # one scalar for all tokens
+        dE, dC = _lib.cce_backward(dloss, E, C, targets, lse, ctx.ignore_index, ctx.filter_eps)
+        return (_to_param_dtype(dE, E) if ctx.needs_input_grad[0] else None,
+                _to_param_dtype(dC, C) if ctx.needs_input_grad[1] else None, None, None, None)
+
+
+class _Mean(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, E, C, targets, ignore_index, filter_eps):
+        mean, n_valid, dE, dC = _lib.cce_loss_mean(E, C, targets, ignore_index, filter_eps)
+        ctx.save_for_backward(dE, dC)
+        ctx.dtypes = (E.dtype, C.dtype)
+        ctx.mark_non_differentiable(n_valid)
+        return mean.reshape(()), n_valid.reshape(())
+
+    @staticmethod
+    def backward(ctx, grad_mean, _grad_n):
+        dE, dC = ctx.saved_tensors
+        g = grad_mean.to(torch.float32)
+        gE = dE.mul(g).to(ctx.dtypes[0]) if ctx.needs_input_grad[0] else None
+        gC = dC.mul(g).to(ctx.dtypes[1]) if ctx.needs_input_grad[1] else None
+        return gE, gC, None, None, None
+
+
+def linear_cross_entropy(E: torch.Tensor, C: torch.Tensor, targets: torch.Tensor,
+                         ignore_index: int = -100, filter_eps: float = FILTER_EPS,
+                         reduction: str = "mean") -> torch.Tensor:
+    """Cross-entropy of the logits E @ C.T against targets, without materialising the logits.
+
+    reduction: "mean" (over non-ignored tokens; 0 when every token is ignored), "sum" or
+    "none" (per-token losses, 0 for ignored tokens).  E, C: CUDA, contiguous, same dtype
+    (bf16 or fp32); targets: int64 [N]."""
+    if reduction == "none":
+        return _PerToken.apply(E, C, targets, int(ignore_index), float(filter_eps))
+    if reduction == "sum":
+        return _Sum.apply(E, C, targets, int(ignore_index), float(filter_eps))
+    if reduction == "mean":
+        mean, _ = _Mean.apply(E, C, targets, int(ignore_index), float(filter_eps))
+        return mean
+    raise ValueError(f"reduction must be 'mean', 'sum' or 'none', not {reduction!r}")
+
+
+class LinearCrossEntropy(torch.nn.Module):
+    """Module form of linear_cross_entropy: forward(E, C, targets)."""
+
+    def __init__(self, ignore_index: int = -100, filter_eps: float = FILTER_EPS,
+                 reduction: str = "mean"):
+        super().__init__()
+        if reduction not in ("mean", "sum", "none"):
+            raise ValueError(f"reduction must be 'mean', 'sum' or 'none', not {reduction!r}")
+        self.ignore_index, self.filter_eps, self.reduction = ignore_index, filter_eps, reduction
+
+    def forward(self, E: torch.Tensor, C: torch.Tensor, targets: torch.Tensor) -> torch.Tensor:
+        return linear_cross_entropy(E, C, targets, self.ignore_index, self.filter_eps,
+                                    self.reduction)
+
+    def extra_repr(self) -> str:
+        return (f"ignore_index={self.ignore_index}, filter_eps={self.filter_eps}, "
+                f"reduction={self.reduction!r}")
