@@ -155,6 +155,59 @@ def copy_calibration() -> int:
     return 0
 
 
+def memory_compare(workload: str) -> int:
+    """Peak device memory and time of one forward + backward of the classifier-head loss at the
+    workload's shape: a plain PyTorch head (logits materialised by a library GEMM, then
+    log-softmax, NLL and autograd's backward) against libcce through its autograd wrapper.
+    Prints one JSON line.  Context for the pages' Gemma 2 (2B) memory figures, not a parity
+    check (their N and hardware are not given)."""
+    import torch
+    import torch.nn.functional as F
+
+    import cce_synth as S
+    from linear_cross_entropy_cce_amd import linear_cross_entropy
+    w = S.WORKLOADS[workload]
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = S.make_inputs(w)
+    E0 = torch.from_numpy(d["E"]).to(dev, tdt)
+    C0 = torch.from_numpy(d["C"]).to(dev, tdt)
+    t = torch.from_numpy(d["targets"]).to(dev)
+
+    def naive(E, C):
+        logits = F.linear(E, C).float()
+        return F.cross_entropy(logits, t, ignore_index=S.IGNORE_INDEX)
+
+    def cce_head(E, C):
+        return linear_cross_entropy(E, C, t, S.IGNORE_INDEX, w.filter_eps, "mean")
+
+    out = {"workload": f"{w.name}: N={w.N} D={w.D} V={w.V} {w.dtype}"}
+    for name, fn in (("pytorch_materialised", naive), ("libcce", cce_head)):
+        E = E0.detach().clone().requires_grad_(True)
+        C = C0.detach().clone().requires_grad_(True)
+        fn(E, C).backward()                      # warm-up (allocator, libraries)
+        E.grad = C.grad = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        t0 = time.perf_counter()
+        loss = fn(E, C)
+        loss.backward()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3
+        peak = torch.cuda.max_memory_allocated() - base
+        grads = E.grad.numel() * E.grad.element_size() + C.grad.numel() * C.grad.element_size()
+        out[name] = {"loss": float(loss.item()), "ms": ms, "peak_bytes_above_inputs": int(peak),
+                     "gradient_bytes": int(grads),
+                     "peak_minus_gradients": int(peak - grads)}
+        del E, C, loss
+    out["ratio_peak_minus_gradients"] = (out["pytorch_materialised"]["peak_minus_gradients"] /
+                                         max(out["libcce"]["peak_minus_gradients"], 1))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +218,9 @@ def main() -> int:
                     help="override the workload's gradient filter threshold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--memory-compare", action="store_true",
+                    help="only compare peak device memory of a materialising PyTorch head with "
+                         "libcce at the workload's shape (one JSON line)")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the GPU clock / power sampling after the timed region")
     ap.add_argument("--no-gemm-ref", action="store_true",
@@ -175,6 +231,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration()
+    if args.memory_compare:
+        return memory_compare(args.workload)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

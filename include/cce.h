@@ -17,7 +17,7 @@
  *   - targets is int64 [N]; a row whose target equals ignore_index is "ignored": its loss is 0,
  *     its gradient rows are 0, and it never makes a filter block significant.
  *   - All array arguments are device pointers into memory the caller owns (hipMalloc or a
- *     framework allocator).  The library never allocates or frees device memory and keeps no
+ *     framework allocator), 16-byte aligned.  The library never allocates or frees device memory and keeps no
  *     per-call state; scratch memory is the caller's workspace (query its size first).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work on
  *     that stream and returns; no host synchronisation happens inside.  Calls that share a
@@ -58,7 +58,9 @@ const char* cce_status_string(cce_status s);
  *   forward : splits * N * 8 bytes, splits <= 256 vocabulary ranges (an on-chip LSE partial
  *             per token and range), rounded to 256 bytes;
  *   backward: 2 * roundup(N,256) * Vc * sizeof(dtype): the softmax-gradient tile store of two
- *             vocabulary chunks in flight (Vc <= 8192 columns), plus their 64x64 block flags;
+ *             vocabulary chunks in flight (Vc <= 8192 columns), plus their 64x64 block flags,
+ *             plus N * D * 4 bytes for the fp32 dE accumulator used when the gradients are
+ *             requested in bf16;
  *   mean    : forward + backward + 8 * roundup(N,64) + 256.
  * Returns 0 for invalid sizes. */
 size_t cce_forward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dtype);
@@ -88,25 +90,28 @@ cce_status cce_forward(const void* E, const void* C, const int64_t* targets,
  *                        0 disables it.  A 64-token x 64-vocabulary block of G is skipped when
  *                        all of its softmax entries are < filter_eps and it holds no target of
  *                        a non-ignored row.  2^-12 is the threshold used by the benchmarks.
- *   dE [N,D], dC [V,D]   fp32, device, overwritten (no need to clear them first).
+ *   dE [N,D], dC [V,D]   device, overwritten (no need to clear them first), in grad_dtype:
+ *                        CCE_F32, or CCE_BF16 (accumulated in fp32, rounded to nearest even
+ *                        once at the end; 16-byte aligned like every array argument).
  *   ws, ws_bytes         device workspace of at least cce_backward_workspace_bytes().
  *   skip_stats           device int64[2] or NULL: [0] = skipped 64x64 blocks,
  *                        [1] = all blocks, ceil(N/64) * ceil(V/64). */
 cce_status cce_backward(const float* dloss, int64_t dloss_stride, const void* E, const void* C,
                         const int64_t* targets, const float* lse, int64_t N, int64_t V,
                         int64_t D, cce_dtype dtype, int64_t ignore_index, float filter_eps,
-                        float* dE, float* dC, void* ws, size_t ws_bytes, int64_t* skip_stats,
-                        void* stream);
+                        void* dE, void* dC, cce_dtype grad_dtype, void* ws, size_t ws_bytes,
+                        int64_t* skip_stats, void* stream);
 
 /* Mean-reduced convenience call: loss_mean = sum over non-ignored rows of loss / N_valid and
  * the gradients of that mean (dloss = 1 / N_valid for every row).  With N_valid == 0 the mean
  * and both gradients are 0.  loss_mean and n_valid (NULL allowed) are device scalars.
+ *   dE, dC, grad_dtype as in cce_backward.
  *   ws: at least cce_loss_mean_workspace_bytes(); err_flag, skip_stats as above. */
 cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, int64_t N,
                          int64_t V, int64_t D, cce_dtype dtype, int64_t ignore_index,
-                         float filter_eps, float* loss_mean, int64_t* n_valid, float* dE,
-                         float* dC, void* ws, size_t ws_bytes, int32_t* err_flag,
-                         int64_t* skip_stats, void* stream);
+                         float filter_eps, float* loss_mean, int64_t* n_valid, void* dE,
+                         void* dC, cce_dtype grad_dtype, void* ws, size_t ws_bytes,
+                         int32_t* err_flag, int64_t* skip_stats, void* stream);
 
 /* Launch-shape introspection for reports (pure host): the vocabulary split count of the
  * forward and the vocabulary chunk width Vc of the backward for a problem. */

@@ -34,9 +34,9 @@ SIGNATURES = {
     "cce_forward": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _c_ptr, _c_ptr,
                            _c_ptr, _sz, _c_ptr, _c_ptr]),
     "cce_backward": (_i32, [_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32,
-                            _i64, _f32, _c_ptr, _c_ptr, _c_ptr, _sz, _c_ptr, _c_ptr]),
+                            _i64, _f32, _c_ptr, _c_ptr, _i32, _c_ptr, _sz, _c_ptr, _c_ptr]),
     "cce_loss_mean": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _f32, _c_ptr,
-                             _c_ptr, _c_ptr, _c_ptr, _c_ptr, _sz, _c_ptr, _c_ptr, _c_ptr]),
+                             _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _sz, _c_ptr, _c_ptr, _c_ptr]),
     "cce_timing_begin": (_i32, [ctypes.c_uint32, ctypes.c_int32]),
     "cce_timing_end": (_i32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int64)]),
 }
@@ -142,9 +142,20 @@ def cce_forward(E, C, targets, ignore_index: int = -100, *, loss=None, lse=None,
     return loss, lse
 
 
+def _grad_outputs(N, V, D, dev, grad_dtype, dE, dC):
+    gdt = torch.float32 if grad_dtype is None else grad_dtype
+    dE = torch.empty((N, D), dtype=gdt, device=dev) if dE is None else dE
+    dC = torch.empty((V, D), dtype=gdt, device=dev) if dC is None else dC
+    for name, g, shape in (("dE", dE, (N, D)), ("dC", dC, (V, D))):
+        if g.dtype != gdt or tuple(g.shape) != shape or not g.is_contiguous() or not g.is_cuda:
+            raise ValueError(f"{name} must be a contiguous {gdt} GPU tensor of shape {shape}")
+    return dE, dC, dtype_code(gdt)
+
+
 def cce_backward(dloss, E, C, targets, lse, ignore_index: int = -100, filter_eps: float = 0.0,
-                 *, dE=None, dC=None, ws=None, skip_stats=None, stream=None):
-    """dE [N,D] and dC [V,D] (fp32).  dloss: fp32 [N], or a 1-element tensor (scalar)."""
+                 *, dE=None, dC=None, grad_dtype=None, ws=None, skip_stats=None, stream=None):
+    """dE [N,D] and dC [V,D] in grad_dtype (torch.float32 by default, or torch.bfloat16).
+    dloss: fp32 [N], or a 1-element tensor (scalar)."""
     N, V, D, dt = _check_inputs(E, C, targets)
     dev = E.device
     if dloss.dtype != torch.float32 or not dloss.is_cuda:
@@ -152,33 +163,32 @@ def cce_backward(dloss, E, C, targets, lse, ignore_index: int = -100, filter_eps
     stride = 0 if dloss.numel() == 1 and N != 1 else 1
     if stride == 1 and dloss.shape != (N,):
         raise ValueError("dloss must have N elements or one")
-    dE = torch.empty((N, D), dtype=torch.float32, device=dev) if dE is None else dE
-    dC = torch.empty((V, D), dtype=torch.float32, device=dev) if dC is None else dC
+    dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
     need = lib().cce_backward_workspace_bytes(N, V, D, dt)
     ws = workspace(need, dev) if ws is None else ws
     _check("cce_backward", lib().cce_backward(
         _ptr(dloss), stride, _ptr(E), _ptr(C), _ptr(targets), _ptr(lse), N, V, D, dt,
-        ignore_index, float(filter_eps), _ptr(dE), _ptr(dC), _ptr(ws),
+        ignore_index, float(filter_eps), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
         ws.numel() * ws.element_size(), _ptr(skip_stats), _stream(stream)))
     return dE, dC
 
 
 def cce_loss_mean(E, C, targets, ignore_index: int = -100, filter_eps: float = 0.0, *,
-                  dE=None, dC=None, ws=None, err_flag=None, skip_stats=None, stream=None):
-    """Mean loss over non-ignored tokens and its gradients.  Returns (mean[1], n_valid[1],
-    dE, dC) as device tensors."""
+                  dE=None, dC=None, grad_dtype=None, ws=None, err_flag=None, skip_stats=None,
+                  stream=None):
+    """Mean loss over non-ignored tokens and its gradients (in grad_dtype, fp32 by default).
+    Returns (mean[1], n_valid[1], dE, dC) as device tensors."""
     N, V, D, dt = _check_inputs(E, C, targets)
     dev = E.device
     mean = torch.empty(1, dtype=torch.float32, device=dev)
     n_valid = torch.empty(1, dtype=torch.int64, device=dev)
-    dE = torch.empty((N, D), dtype=torch.float32, device=dev) if dE is None else dE
-    dC = torch.empty((V, D), dtype=torch.float32, device=dev) if dC is None else dC
+    dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
     need = lib().cce_loss_mean_workspace_bytes(N, V, D, dt)
     ws = workspace(need, dev) if ws is None else ws
     _check("cce_loss_mean", lib().cce_loss_mean(
         _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, float(filter_eps),
-        _ptr(mean), _ptr(n_valid), _ptr(dE), _ptr(dC), _ptr(ws), ws.numel() * ws.element_size(),
-        _ptr(err_flag), _ptr(skip_stats), _stream(stream)))
+        _ptr(mean), _ptr(n_valid), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
+        ws.numel() * ws.element_size(), _ptr(err_flag), _ptr(skip_stats), _stream(stream)))
     return mean, n_valid, dE, dC
 
 

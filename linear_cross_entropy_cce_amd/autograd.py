@@ -10,12 +10,13 @@ backward skips 64 x 64 blocks of the softmax gradient whose entries are all belo
 (sentence 9; 0 disables it).
 
 Every step of the computation runs in libcce's kernels (cce_forward / cce_backward /
-cce_loss_mean); this module only routes tensors and gradients:
+cce_loss_mean, which return the gradients in the dtype of E and C, accumulated in fp32); this
+module only routes tensors and gradients:
   * "none": per-token losses; the backward passes the upstream gradient as libcce's dloss;
   * "sum":  the per-token losses summed (dloss = the upstream scalar for every token);
   * "mean": libcce's mean call, which returns the mean over non-ignored tokens together with
-    its gradients in one pass; the backward scales them by the upstream scalar.
-Gradients come back in the dtype of E and C (libcce computes them in fp32).
+    its gradients in one pass; the backward scales them in place by the upstream scalar (so
+    it runs once per forward).
 """
 from __future__ import annotations
 
@@ -24,10 +25,6 @@ import torch
 from . import _lib
 
 FILTER_EPS = 2.0 ** -12
-
-
-def _to_param_dtype(g: torch.Tensor, like: torch.Tensor) -> torch.Tensor:
-    return g if g.dtype == like.dtype else g.to(like.dtype)
 
 
 class _PerToken(torch.autograd.Function):
@@ -45,9 +42,10 @@ class _PerToken(torch.autograd.Function):
         if not (ctx.needs_input_grad[0] or ctx.needs_input_grad[1]):
             return None, None, None, None, None
         dloss = grad_loss.to(torch.float32).contiguous()
-        dE, dC = _lib.cce_backward(dloss, E, C, targets, lse, ctx.ignore_index, ctx.filter_eps)
-        return (_to_param_dtype(dE, E) if ctx.needs_input_grad[0] else None,
-                _to_param_dtype(dC, C) if ctx.needs_input_grad[1] else None, None, None, None)
+        dE, dC = _lib.cce_backward(dloss, E, C, targets, lse, ctx.ignore_index, ctx.filter_eps,
+                                   grad_dtype=E.dtype)
+        return (dE if ctx.needs_input_grad[0] else None,
+                dC if ctx.needs_input_grad[1] else None, None, None, None)
 
 
 class _Sum(torch.autograd.Function):
@@ -65,26 +63,34 @@ class _Sum(torch.autograd.Function):
         if not (ctx.needs_input_grad[0] or ctx.needs_input_grad[1]):
             return None, None, None, None, None
         dloss = grad_sum.to(torch.float32).reshape(1).contiguous()   # one scalar for all tokens
-        dE, dC = _lib.cce_backward(dloss, E, C, targets, lse, ctx.ignore_index, ctx.filter_eps)
-        return (_to_param_dtype(dE, E) if ctx.needs_input_grad[0] else None,
-                _to_param_dtype(dC, C) if ctx.needs_input_grad[1] else None, None, None, None)
+        dE, dC = _lib.cce_backward(dloss, E, C, targets, lse, ctx.ignore_index, ctx.filter_eps,
+                                   grad_dtype=E.dtype)
+        return (dE if ctx.needs_input_grad[0] else None,
+                dC if ctx.needs_input_grad[1] else None, None, None, None)
 
 
 class _Mean(torch.autograd.Function):
     @staticmethod
     def forward(ctx, E, C, targets, ignore_index, filter_eps):
-        mean, n_valid, dE, dC = _lib.cce_loss_mean(E, C, targets, ignore_index, filter_eps)
+        mean, n_valid, dE, dC = _lib.cce_loss_mean(E, C, targets, ignore_index, filter_eps,
+                                                   grad_dtype=E.dtype)
         ctx.save_for_backward(dE, dC)
-        ctx.dtypes = (E.dtype, C.dtype)
         ctx.mark_non_differentiable(n_valid)
         return mean.reshape(()), n_valid.reshape(())
 
     @staticmethod
     def backward(ctx, grad_mean, _grad_n):
+        # The gradients computed by the forward are scaled in place (no second copy of dC),
+        # so this backward can run once per forward.
+        if getattr(ctx, "used", False):
+            raise RuntimeError("linear_cross_entropy(reduction='mean') supports one backward "
+                               "per forward; use reduction='sum' or 'none' to differentiate "
+                               "the same graph twice")
+        ctx.used = True
         dE, dC = ctx.saved_tensors
-        g = grad_mean.to(torch.float32)
-        gE = dE.mul(g).to(ctx.dtypes[0]) if ctx.needs_input_grad[0] else None
-        gC = dC.mul(g).to(ctx.dtypes[1]) if ctx.needs_input_grad[1] else None
+        g = grad_mean.to(dE.dtype)
+        gE = dE.mul_(g) if ctx.needs_input_grad[0] else None
+        gC = dC.mul_(g) if ctx.needs_input_grad[1] else None
         return gE, gC, None, None, None
 
 

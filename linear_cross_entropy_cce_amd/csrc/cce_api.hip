@@ -88,18 +88,22 @@ int64_t plan_chunk(int64_t V) {
   return std::min<int64_t>(vc, ceil_div(V, kTile) * kTile);
 }
 
+// Backward workspace: G and flags of two chunks in flight (c and c + 1), then the fp32 dE
+// accumulator used when the gradients are requested in bf16.
 struct BwdLayout {
   int64_t n_pad, vc, fstride;
-  size_t g_bytes, flag_bytes, total;
+  size_t g_bytes, flag_bytes, acc_offset, acc_bytes, total;
 };
-BwdLayout bwd_layout(int64_t N, int64_t V, cce_dtype dt) {
+BwdLayout bwd_layout(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
   BwdLayout L;
   L.n_pad = ceil_div(std::max<int64_t>(N, 1), kTile) * kTile;
   L.vc = plan_chunk(V);
   L.fstride = L.vc / 64;
   L.g_bytes = align_up((size_t)L.n_pad * (size_t)L.vc * dtype_size(dt));
   L.flag_bytes = align_up((size_t)(L.n_pad / 64) * (size_t)L.fstride);
-  L.total = 2 * (L.g_bytes + L.flag_bytes);   // two chunks in flight: c and c + 1
+  L.acc_offset = 2 * (L.g_bytes + L.flag_bytes);
+  L.acc_bytes = align_up((size_t)std::max<int64_t>(N, 1) * (size_t)D * 4);
+  L.total = L.acc_offset + L.acc_bytes;
   return L;
 }
 size_t fwd_bytes(int64_t N, int64_t V) {
@@ -176,9 +180,11 @@ cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, i
 template <typename T>
 cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const T* C,
                          const int64_t* tgt, const float* lse, int64_t N, int64_t V, int64_t D,
-                         int64_t ii, float eps, float* dE, float* dC, void* ws,
+                         int64_t ii, float eps, void* dE, void* dC, cce_dtype gdt, void* ws,
                          int64_t* skip_stats, hipStream_t st, cce_dtype dt) {
-  const BwdLayout L = bwd_layout(N, V, dt);
+  const BwdLayout L = bwd_layout(N, V, D, dt);
+  // dE accumulates over the chunks in fp32: in place, or in the workspace for bf16 output
+  float* dE_acc = gdt == CCE_F32 ? (float*)dE : (float*)((char*)ws + L.acc_offset);
   const int64_t n_tb = L.n_pad / kTile, n_dt = ceil_div(D, kTile);
   const int64_t n_chunks = ceil_div(V, L.vc);
   if (skip_stats) {
@@ -202,7 +208,7 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
     A.fstride = (int)L.fstride;
     A.eps = eps; A.ignore_index = ii;
     A.skip_count = (unsigned long long*)skip_stats;
-    A.dE = dE; A.dC = dC;
+    A.dE = dE_acc; A.dC = dC; A.dc_bf16 = gdt == CCE_BF16 ? 1 : 0;
     A.accumulate = c > 0 ? 1 : 0;
     return A;
   };
@@ -233,6 +239,13 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
                          r_de, r_dc);
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   }
+  if (gdt == CCE_BF16) {
+    TimedLaunch tl(CCE_KERNEL_AUX, st);
+    const int64_t n = N * D;
+    hipLaunchKernelGGL(k_f32_to_bf16, dim3((unsigned)std::min<int64_t>(ceil_div(n, 1024), 4096)),
+                       dim3(256), 0, st, (const float*)dE_acc, (__bf16*)dE, n);
+    if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+  }
   return CCE_OK;
 }
 
@@ -258,12 +271,12 @@ size_t cce_forward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dt
 
 size_t cce_backward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
   if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
-  return bwd_layout(N, V, dt).total;
+  return bwd_layout(N, V, D, dt).total;
 }
 
 size_t cce_loss_mean_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
   if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
-  return fwd_bytes(N, V) + bwd_layout(N, V, dt).total + mean_extra_bytes(N);
+  return fwd_bytes(N, V) + bwd_layout(N, V, D, dt).total + mean_extra_bytes(N);
 }
 
 int64_t cce_forward_splits(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
@@ -295,19 +308,20 @@ cce_status cce_forward(const void* E, const void* C, const int64_t* targets, int
 cce_status cce_backward(const float* dloss, int64_t dloss_stride, const void* E, const void* C,
                         const int64_t* targets, const float* lse, int64_t N, int64_t V,
                         int64_t D, cce_dtype dt, int64_t ignore_index, float filter_eps,
-                        float* dE, float* dC, void* ws, size_t ws_bytes, int64_t* skip_stats,
-                        void* stream) {
+                        void* dE, void* dC, cce_dtype grad_dtype, void* ws, size_t ws_bytes,
+                        int64_t* skip_stats, void* stream) {
   if (!sizes_ok(N, V, D, dt)) return CCE_ERR_INVALID_ARGUMENT;
   if (!sizes_supported(N, V, D)) return CCE_ERR_UNSUPPORTED;
   if (!std::isfinite(filter_eps) || filter_eps < 0.f) return CCE_ERR_INVALID_ARGUMENT;
   if (dloss_stride != 0 && dloss_stride != 1) return CCE_ERR_INVALID_ARGUMENT;
+  if (grad_dtype != CCE_F32 && grad_dtype != CCE_BF16) return CCE_ERR_INVALID_ARGUMENT;
   if (N == 0) {
     // nothing to reduce: dC is still defined (all zero) and so are the statistics
     if (!dC) return CCE_ERR_INVALID_ARGUMENT;
     hipStream_t st = (hipStream_t)stream;
-    const int64_t n = V * D;
+    const int64_t n = V * D * (int64_t)dtype_size(grad_dtype) / 4;   // 4-byte words
     hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)std::min<int64_t>(ceil_div(n, 1024), 4096)),
-                       dim3(256), 0, st, dC, n);
+                       dim3(256), 0, st, (float*)dC, n);
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
     if (skip_stats) {
       hipLaunchKernelGGL(k_skip_init, dim3(1), dim3(64), 0, st, skip_stats, (int64_t)0);
@@ -317,22 +331,22 @@ cce_status cce_backward(const float* dloss, int64_t dloss_stride, const void* E,
   }
   if (!dloss || !E || !C || !targets || !lse || !dE || !dC || !ws)
     return CCE_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < bwd_layout(N, V, dt).total) return CCE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < bwd_layout(N, V, D, dt).total) return CCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   if (dt == CCE_BF16)
     return backward_impl<__bf16>(dloss, dloss_stride, (const __bf16*)E, (const __bf16*)C,
-                                 targets, lse, N, V, D, ignore_index, filter_eps, dE, dC, ws,
-                                 skip_stats, st, dt);
+                                 targets, lse, N, V, D, ignore_index, filter_eps, dE, dC,
+                                 grad_dtype, ws, skip_stats, st, dt);
   return backward_impl<float>(dloss, dloss_stride, (const float*)E, (const float*)C, targets,
-                              lse, N, V, D, ignore_index, filter_eps, dE, dC, ws, skip_stats,
-                              st, dt);
+                              lse, N, V, D, ignore_index, filter_eps, dE, dC, grad_dtype, ws,
+                              skip_stats, st, dt);
 }
 
 cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, int64_t N,
                          int64_t V, int64_t D, cce_dtype dt, int64_t ignore_index,
-                         float filter_eps, float* loss_mean, int64_t* n_valid, float* dE,
-                         float* dC, void* ws, size_t ws_bytes, int32_t* err_flag,
-                         int64_t* skip_stats, void* stream) {
+                         float filter_eps, float* loss_mean, int64_t* n_valid, void* dE,
+                         void* dC, cce_dtype grad_dtype, void* ws, size_t ws_bytes,
+                         int32_t* err_flag, int64_t* skip_stats, void* stream) {
   if (!sizes_ok(N, V, D, dt)) return CCE_ERR_INVALID_ARGUMENT;
   if (!sizes_supported(N, V, D)) return CCE_ERR_UNSUPPORTED;
   if (!std::isfinite(filter_eps) || filter_eps < 0.f) return CCE_ERR_INVALID_ARGUMENT;
@@ -340,7 +354,8 @@ cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, i
   if (N > 0 && (!E || !C || !targets || !dE)) return CCE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < cce_loss_mean_workspace_bytes(N, V, D, dt)) return CCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
-  const size_t fb = fwd_bytes(N, V), bb = bwd_layout(N, V, dt).total;
+  if (grad_dtype != CCE_F32 && grad_dtype != CCE_BF16) return CCE_ERR_INVALID_ARGUMENT;
+  const size_t fb = fwd_bytes(N, V), bb = bwd_layout(N, V, D, dt).total;
   char* base = (char*)ws;
   char* extra = base + fb + bb;
   const size_t rows = (size_t)ceil_div(std::max<int64_t>(N, 1), 64) * 64;
@@ -352,7 +367,7 @@ cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, i
                        (const int64_t*)nullptr, 0, ignore_index, loss_mean, dloss, n_valid);
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
     return cce_backward(dloss, 0, E, C, targets, lse, 0, V, D, dt, ignore_index, filter_eps,
-                        dE, dC, base + fb, bb, skip_stats, stream);
+                        dE, dC, grad_dtype, base + fb, bb, skip_stats, stream);
   }
   cce_status s = cce_forward(E, C, targets, N, V, D, dt, ignore_index, loss, lse, base, fb,
                              err_flag, stream);
@@ -364,7 +379,7 @@ cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, i
   }
   if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   return cce_backward(dloss, 0, E, C, targets, lse, N, V, D, dt, ignore_index, filter_eps, dE,
-                      dC, base + fb, bb, skip_stats, stream);
+                      dC, grad_dtype, base + fb, bb, skip_stats, stream);
 }
 
 cce_status cce_timing_begin(uint32_t kind_mask, int32_t max_launches) {

@@ -283,8 +283,9 @@ struct BwdArgs {
   float eps;
   int64_t ignore_index;
   unsigned long long* skip_count;
-  float* dE;                  // [N, D]
-  float* dC;                  // [V, D]
+  float* dE;                  // [N, D] fp32 accumulator of dE over the chunks
+  void* dC;                   // [V, D] in the gradient dtype
+  int dc_bf16;                // dC written as bf16 (else fp32)
   int accumulate;             // dE += (later chunks) instead of dE = (first chunk)
 };
 
@@ -449,6 +450,24 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
         }
       }
     }
+}
+
+// Writes this wave's 128 x 64 accumulators to a row-major bf16 matrix out[rows][ld] at
+// (row0, col0), rounding to nearest even; rows >= row_lim and columns >= col_lim are dropped.
+__device__ __forceinline__ void store_tile_bf16(__bf16* __restrict__ out, int64_t ld, int row0,
+                                                int row_lim, int col0, int col_lim, Acc& acc,
+                                                int lane) {
+  const bool full = row0 + kWaveM <= row_lim && col0 + kWaveN <= col_lim;
+#pragma unroll
+  for (int mi = 0; mi < kMB; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNB; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + 32 * mi + acc_row(r, lane), col = col0 + 32 * ni + (lane & 31);
+        if (full || (row < row_lim && col < col_lim))
+          out[(int64_t)row * ld + col] = (__bf16)acc[mi][ni][r];
+      }
 }
 
 // Writes (or adds) this wave's 128 x 64 accumulators to a row-major fp32 matrix out[rows][ld]
@@ -623,7 +642,7 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
   const int D = A.D, N = A.N, n_pad = A.n_pad, vc = A.vc, n_vtc = A.n_vtc, n_dt = A.n_dt;
   const uint8_t* __restrict__ flags = A.flags;
   const int fstride = A.fstride;
-  float* __restrict__ dCc = A.dC + (int64_t)A.v0 * A.D;
+  const int64_t dc_off = (int64_t)A.v0 * A.D;
   int vt, dt;
   grouped_tile(lin, n_vtc, n_dt, vt, dt);
   if (vt >= n_vtc || dt >= n_dt) return;
@@ -661,7 +680,12 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
     }
     __syncthreads();
   }
-  store_tile(dCc, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc, lane, false);
+  if (A.dc_bf16)
+    store_tile_bf16((__bf16*)A.dC + dc_off, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc,
+                    lane);
+  else
+    store_tile((float*)A.dC + dc_off, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc, lane,
+               false);
 }
 
 // Work items of the backward launches: one per tile (grouped_tile).
@@ -701,6 +725,19 @@ __global__ void k_zero_f32(float* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0.f;
+}
+
+// out[i] = bf16(in[i]) (round to nearest even), 4 elements per thread and step (n % 4 == 0).
+__global__ void k_f32_to_bf16(const float* __restrict__ in, __bf16* __restrict__ out, int64_t n) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n;
+       i += (int64_t)gridDim.x * blockDim.x * 4) {
+    const f32x4_t v = *(const f32x4_t*)(in + i);
+    bf16x4_t o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = (__bf16)v[k];
+    *(bf16x4_t*)(out + i) = o;
+  }
 }
 
 // skip_stats = {0, total}

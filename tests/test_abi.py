@@ -47,7 +47,7 @@ def test_status_strings(lib):
 def test_workspace_has_no_tokens_times_vocabulary_term(lib, dt):
     """Extra device bytes are bounded by a per-token constant that does not grow with V:
     forward <= 8 bytes x 256 ranges per token, backward <= two chunks of 8192 vocabulary
-    columns of G per (padded) token plus their block flags."""
+    columns of G per (padded) token plus their block flags, plus an fp32 dE accumulator."""
     sz = 4 if dt == 0 else 2
     for V, D in ((256000, 2304), (128256, 4096), (32000, 2048), (1000, 64), (10 ** 6, 64)):
         for N in (1, 255, 4096, 8192, 65536):
@@ -56,12 +56,25 @@ def test_workspace_has_no_tokens_times_vocabulary_term(lib, dt):
             bb = lib.cce_backward_workspace_bytes(N, V, D, dt)
             mb = lib.cce_loss_mean_workspace_bytes(N, V, D, dt)
             assert 0 < fb <= 2048 * N + 256
-            assert 0 < bb <= 2 * (pad * 8192 * sz + pad * 2 + 256)
+            assert 0 < bb <= 2 * (pad * 8192 * sz + pad * 2 + 256) + N * D * 4 + 256
             assert fb + bb < mb <= fb + bb + 8 * (N + 64) + 512
     # the logits of one config-sized problem would be 4 N V bytes; the workspace is far below
     N, V, D = 8192, 256000, 2304
     total = lib.cce_loss_mean_workspace_bytes(N, V, D, 1)
-    assert total < 4 * N * V / 25
+    assert total < 4 * N * V / 20
+
+
+@pytest.mark.parametrize("dt", [0, 1])
+def test_backward_workspace_is_affine_in_tokens(lib, dt):
+    """Sweep N over multiples of the 256-token tile at fixed V and D: the backward workspace
+    is exactly a + b N, and the slope b does not grow with V (no N x V term)."""
+    slopes = {}
+    for V in (32000, 256000, 10 ** 6):
+        ws = [lib.cce_backward_workspace_bytes(N, V, 2304, dt) for N in (2048, 4096, 8192, 16384)]
+        d1, d2, d3 = ws[1] - ws[0], ws[2] - ws[1], ws[3] - ws[2]
+        assert d2 == 2 * d1 and d3 == 2 * d2
+        slopes[V] = d1 / 2048
+    assert slopes[256000] == slopes[10 ** 6]      # chunk width capped: per-token bytes fixed
 
 
 def test_plan_introspection(lib):
@@ -105,9 +118,10 @@ def test_forward_validation(lib):
 def test_backward_validation(lib):
     ok_ws = lib.cce_backward_workspace_bytes(16, 100, 64, 1)
     base = dict(dl=_fake(9), stride=1, E=_fake(1), C=_fake(2), t=_fake(3), lse=_fake(4), N=16,
-                V=100, D=64, dt=1, ii=-100, eps=0.0, dE=_fake(5), dC=_fake(6), ws=_fake(7),
-                wsb=ok_ws, sk=None, st=None)
+                V=100, D=64, dt=1, ii=-100, eps=0.0, dE=_fake(5), dC=_fake(6), gdt=0,
+                ws=_fake(7), wsb=ok_ws, sk=None, st=None)
     call = lambda **k: lib.cce_backward(*dict(base, **k).values())
+    assert call(gdt=2) == 1
     assert call(eps=-1.0) == 1
     assert call(eps=float("inf")) == 1
     assert call(eps=float("nan")) == 1
@@ -121,9 +135,10 @@ def test_backward_validation(lib):
 def test_loss_mean_validation(lib):
     ok_ws = lib.cce_loss_mean_workspace_bytes(16, 100, 64, 1)
     base = dict(E=_fake(1), C=_fake(2), t=_fake(3), N=16, V=100, D=64, dt=1, ii=-100, eps=0.0,
-                mean=_fake(4), nv=None, dE=_fake(5), dC=_fake(6), ws=_fake(7), wsb=ok_ws,
-                err=None, sk=None, st=None)
+                mean=_fake(4), nv=None, dE=_fake(5), dC=_fake(6), gdt=1, ws=_fake(7),
+                wsb=ok_ws, err=None, sk=None, st=None)
     call = lambda **k: lib.cce_loss_mean(*dict(base, **k).values())
+    assert call(gdt=-1) == 1
     assert call(mean=None) == 1
     assert call(wsb=ok_ws - 1) == 3
     assert call(eps=-0.5) == 1

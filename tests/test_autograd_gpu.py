@@ -44,9 +44,20 @@ def test_autograd_gradients_match_oracle(reduction):
         assert abs(float(got) - loss.sum()) <= LOSS_TOL * N
     else:
         assert abs(float(got) - loss.sum() / n_valid) <= LOSS_TOL
-    # bf16 gradients: one more rounding (2^-9 relative) on top of the kernel's error
+    # bf16 gradients (libcce rounds its fp32 results once): 2^-9 relative on top of the
+    # kernel's error
     assert rel(E.grad.float().cpu().numpy(), dE) <= GRAD_TOL
     assert rel(C.grad.float().cpu().numpy(), dC) <= GRAD_TOL
+
+
+def test_mean_backward_runs_once():
+    d = S.small_case(64, 64, 300, "bf16", 104, 3.0, 1.1, 0.0)
+    E0, C0, t = upload(d, "bf16")
+    C = _leaf(C0)
+    loss = linear_cross_entropy(E0, C, t, II, EPS, "mean")
+    loss.backward(retain_graph=True)
+    with pytest.raises(RuntimeError, match="one backward"):
+        loss.backward()
 
 
 def test_module_and_partial_requires_grad():

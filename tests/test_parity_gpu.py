@@ -172,3 +172,38 @@ def test_loss_mean_all_ignored_is_zero():
     torch.cuda.synchronize()
     assert float(mean.item()) == 0.0 and int(nv.item()) == 0
     assert float(dE.abs().max()) == 0.0 and float(dC.abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bf16_gradients_are_the_rounded_fp32_gradients(dtype):
+    """grad_dtype = bf16: both gradients are the fp32 results rounded to nearest even, bit for
+    bit (same kernels and order; dE rounded once after the last chunk)."""
+    d = S.small_case(300, 72, 20000, dtype, 111, 3.0, 1.1, 0.1)
+    log(f"[bf16 grads] {dtype}")
+    E, C, t = upload(d, dtype)
+    loss, lse = cce.cce_forward(E, C, t, II)
+    dl = torch.from_numpy(S.dloss_weights(111, 300)).to(DEV)
+    e32, c32 = cce.cce_backward(dl, E, C, t, lse, II, EPS)
+    e16, c16 = cce.cce_backward(dl, E, C, t, lse, II, EPS, grad_dtype=torch.bfloat16)
+    mean, nv, me16, mc16 = cce.cce_loss_mean(E, C, t, II, EPS, grad_dtype=torch.bfloat16)
+    _, _, me32, mc32 = cce.cce_loss_mean(E, C, t, II, EPS)
+    torch.cuda.synchronize()
+    assert e16.dtype == torch.bfloat16 and c16.dtype == torch.bfloat16
+    assert torch.equal(e16, e32.to(torch.bfloat16)) and torch.equal(c16, c32.to(torch.bfloat16))
+    assert torch.equal(me16, me32.to(torch.bfloat16)) and torch.equal(mc16, mc32.to(torch.bfloat16))
+    rE, rC, _ = oracle.backward(d["E"], d["C"], d["targets"], S.dloss_weights(111, 300), II,
+                                filter_eps=EPS)
+    assert rel(e16.float().cpu().numpy(), rE) <= GRAD_TOL
+    assert rel(c16.float().cpu().numpy(), rC) <= GRAD_TOL
+
+
+def test_empty_batch_bf16_gradients():
+    E = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    C = torch.randn((300, 64), device=DEV).to(torch.bfloat16)
+    t = torch.zeros(0, dtype=torch.int64, device=DEV)
+    loss, lse = cce.cce_forward(E, C, t)
+    dC = torch.full((300, 64), 7.0, device=DEV, dtype=torch.bfloat16)
+    dE, dC = cce.cce_backward(torch.ones(0, device=DEV), E, C, t, lse, dC=dC,
+                              grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert dE.numel() == 0 and float(dC.float().abs().max()) == 0.0
