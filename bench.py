@@ -208,6 +208,56 @@ def memory_compare(workload: str) -> int:
     return 0
 
 
+def shards_compare(workload: str, n_shards: int, steps: int, warmup: int) -> int:
+    """The vocabulary-sharded head emulated on one GPU (one JSON line): a fwd+bwd step through
+    S shards of C (cce_forward_shard per shard, cce_merge_shards, cce_backward_shard per shard
+    with the merged LSE, dE terms summed) against the unsharded step, and the per-shard kernel
+    times, i.e. the work of one device of an S-way tensor-parallel head at its real shape."""
+    import torch
+
+    import cce_synth as S
+    import linear_cross_entropy_cce_amd as cce
+    from linear_cross_entropy_cce_amd import sharded
+    w = S.WORKLOADS[workload]
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = S.make_inputs(w)
+    E = torch.from_numpy(d["E"]).to(dev, tdt)
+    C = torch.from_numpy(d["C"]).to(dev, tdt)
+    t = torch.from_numpy(d["targets"]).to(dev)
+    dl = torch.full((w.N,), 1.0 / w.N, dtype=torch.float32, device=dev)
+    bounds = sharded.shard_bounds(w.V, n_shards)
+
+    def sharded_step():
+        return sharded.forward_backward(E, C, t, bounds, S.IGNORE_INDEX, w.filter_eps, dloss=dl)
+
+    def plain_step():
+        loss, lse = cce.cce_forward(E, C, t, S.IGNORE_INDEX)
+        return cce.cce_backward(dl, E, C, t, lse, S.IGNORE_INDEX, w.filter_eps)
+
+    out = {"workload": f"{w.name}: N={w.N} D={w.D} V={w.V} {w.dtype}", "shards": n_shards,
+           "shard_rows": [b - a for a, b in zip(bounds, bounds[1:])]}
+    for name, fn in (("unsharded", plain_step), ("sharded", sharded_step)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        cce.timing_begin(max_launches=steps * (60 * n_shards + 200))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        k = cce.timing_end()
+        out[name] = {"ms_per_step": a.elapsed_time(b) / steps,
+                     "kernel_ms_per_step": {kk: v[0] / steps for kk, v in k.items()}}
+    sh = out["sharded"]["kernel_ms_per_step"]
+    out["per_shard_ms"] = {"forward": (sh.get("fwd_lse", 0.0) + sh.get("fwd_finish", 0.0)) / n_shards,
+                           "backward": (sh.get("bwd_g", 0.0) + sh.get("bwd_fused", 0.0)) / n_shards}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,6 +268,9 @@ def main() -> int:
                     help="override the workload's gradient filter threshold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--shards", type=int, default=0,
+                    help="only time the vocabulary-sharded head emulated on one GPU with this "
+                         "many shards against the unsharded step (one JSON line)")
     ap.add_argument("--memory-compare", action="store_true",
                     help="only compare peak device memory of a materialising PyTorch head with "
                          "libcce at the workload's shape (one JSON line)")
@@ -233,6 +286,8 @@ def main() -> int:
         return copy_calibration()
     if args.memory_compare:
         return memory_compare(args.workload)
+    if args.shards:
+        return shards_compare(args.workload, args.shards, args.steps, args.warmup)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -113,6 +113,46 @@ cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, i
                          void* dC, cce_dtype grad_dtype, void* ws, size_t ws_bytes,
                          int32_t* err_flag, int64_t* skip_stats, void* stream);
 
+/* Vocabulary-sharded form of the same computation (the tensor-parallel classifier head: each
+ * device holds rows [vocab_offset, vocab_offset + V) of the full classifier, V_total rows in
+ * all).  The log-sum-exp over the full vocabulary is the log-sum-exp of the shards' LSEs (the
+ * abstract's on-the-fly log-sum-exp, sentence 5, split over devices), so a forward is one
+ * cce_forward_shard per shard, an exchange of 2 floats per token and shard, and one
+ * cce_merge_shards; the backward is one cce_backward_shard per shard with the merged LSE, each
+ * giving its shard's rows of dC and a partial dE that the shards sum.
+ *
+ * cce_forward_shard: E [N,D], C [V,D] = this shard's rows, targets [N] in the full vocabulary.
+ *   lse_shard [N]     fp32, device, written: log sum over this shard's rows of exp(E C^T).
+ *   target_logit [N]  fp32, device, written: E[n] . C[t[n] - vocab_offset] when the target is
+ *                     one of this shard's rows (and not ignore_index), else 0.
+ *   ws, ws_bytes      at least cce_forward_workspace_bytes(N, V, D, dtype).
+ *   Targets outside the shard are not errors here; cce_merge_shards checks them. */
+cce_status cce_forward_shard(const void* E, const void* C, const int64_t* targets, int64_t N,
+                             int64_t V, int64_t D, cce_dtype dtype, int64_t ignore_index,
+                             int64_t vocab_offset, float* lse_shard, float* target_logit,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* cce_merge_shards: lse_shards [n_shards][N] and target_logits [n_shards][N] (fp32, device,
+ * shard-major), as written by cce_forward_shard for shards that together cover [0, V_total)
+ * once.  Writes lse [N] and loss [N] exactly as cce_forward does (loss 0 for ignored rows; a
+ * target outside [0, V_total) gives NaN and sets *err_flag to 1 when err_flag is non-NULL).
+ * No workspace. */
+cce_status cce_merge_shards(const float* lse_shards, const float* target_logits,
+                            int64_t n_shards, int64_t N, const int64_t* targets,
+                            int64_t ignore_index, int64_t V_total, float* loss, float* lse,
+                            int32_t* err_flag, void* stream);
+
+/* cce_backward_shard: cce_backward for one shard.  lse [N] is the merged (full-vocabulary) LSE;
+ * dC [V,D] receives this shard's rows of dC; dE [N,D] receives this shard's term of dE (the
+ * shards' dE sum to the full dE).  Filter blocks are aligned to the shard's rows (64-row blocks
+ * from vocab_offset).  Workspace: cce_backward_workspace_bytes(N, V, D, dtype). */
+cce_status cce_backward_shard(const float* dloss, int64_t dloss_stride, const void* E,
+                              const void* C, const int64_t* targets, const float* lse,
+                              int64_t N, int64_t V, int64_t D, cce_dtype dtype,
+                              int64_t ignore_index, int64_t vocab_offset, float filter_eps,
+                              void* dE, void* dC, cce_dtype grad_dtype, void* ws,
+                              size_t ws_bytes, int64_t* skip_stats, void* stream);
+
 /* Launch-shape introspection for reports (pure host): the vocabulary split count of the
  * forward and the vocabulary chunk width Vc of the backward for a problem. */
 int64_t cce_forward_splits(int64_t N, int64_t V, int64_t D, cce_dtype dtype);

@@ -37,6 +37,13 @@ SIGNATURES = {
                             _i64, _f32, _c_ptr, _c_ptr, _i32, _c_ptr, _sz, _c_ptr, _c_ptr]),
     "cce_loss_mean": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _f32, _c_ptr,
                              _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _sz, _c_ptr, _c_ptr, _c_ptr]),
+    "cce_forward_shard": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _i64,
+                                 _c_ptr, _c_ptr, _c_ptr, _sz, _c_ptr]),
+    "cce_merge_shards": (_i32, [_c_ptr, _c_ptr, _i64, _i64, _c_ptr, _i64, _i64, _c_ptr, _c_ptr,
+                                _c_ptr, _c_ptr]),
+    "cce_backward_shard": (_i32, [_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64,
+                                  _i32, _i64, _i64, _f32, _c_ptr, _c_ptr, _i32, _c_ptr, _sz,
+                                  _c_ptr, _c_ptr]),
     "cce_timing_begin": (_i32, [ctypes.c_uint32, ctypes.c_int32]),
     "cce_timing_end": (_i32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int64)]),
 }
@@ -190,6 +197,62 @@ def cce_loss_mean(E, C, targets, ignore_index: int = -100, filter_eps: float = 0
         _ptr(mean), _ptr(n_valid), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
         ws.numel() * ws.element_size(), _ptr(err_flag), _ptr(skip_stats), _stream(stream)))
     return mean, n_valid, dE, dC
+
+
+def cce_forward_shard(E, C_shard, targets, vocab_offset: int, ignore_index: int = -100, *,
+                      lse=None, target_logit=None, ws=None, stream=None):
+    """One vocabulary shard's forward: (lse over the shard's rows, target logit or 0), fp32 [N].
+    targets index the full vocabulary; C_shard holds rows [vocab_offset, vocab_offset + V)."""
+    N, V, D, dt = _check_inputs(E, C_shard, targets)
+    dev = E.device
+    lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else lse
+    zt = torch.empty(N, dtype=torch.float32, device=dev) if target_logit is None else target_logit
+    need = lib().cce_forward_workspace_bytes(N, V, D, dt)
+    ws = workspace(need, dev) if ws is None else ws
+    _check("cce_forward_shard", lib().cce_forward_shard(
+        _ptr(E), _ptr(C_shard), _ptr(targets), N, V, D, dt, ignore_index, int(vocab_offset),
+        _ptr(lse), _ptr(zt), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return lse, zt
+
+
+def cce_merge_shards(lse_shards, target_logits, targets, V_total: int, ignore_index: int = -100,
+                     *, loss=None, lse=None, err_flag=None, stream=None):
+    """Merges [S, N] per-shard LSEs and target logits into (loss, lse), fp32 [N]."""
+    S, N = lse_shards.shape
+    for name, t in (("lse_shards", lse_shards), ("target_logits", target_logits)):
+        if t.dtype != torch.float32 or t.shape != (S, N) or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor [S, N]")
+    if targets.dtype != torch.int64 or targets.shape != (N,) or not targets.is_cuda:
+        raise ValueError("targets must be int64 [N] on the GPU")
+    dev = lse_shards.device
+    loss = torch.empty(N, dtype=torch.float32, device=dev) if loss is None else loss
+    lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else lse
+    _check("cce_merge_shards", lib().cce_merge_shards(
+        _ptr(lse_shards), _ptr(target_logits), S, N, _ptr(targets), ignore_index, int(V_total),
+        _ptr(loss), _ptr(lse), _ptr(err_flag), _stream(stream)))
+    return loss, lse
+
+
+def cce_backward_shard(dloss, E, C_shard, targets, lse, vocab_offset: int,
+                       ignore_index: int = -100, filter_eps: float = 0.0, *, dE=None, dC=None,
+                       grad_dtype=None, ws=None, skip_stats=None, stream=None):
+    """One vocabulary shard's backward with the merged LSE: (this shard's term of dE, the
+    shard's rows of dC)."""
+    N, V, D, dt = _check_inputs(E, C_shard, targets)
+    dev = E.device
+    if dloss.dtype != torch.float32 or not dloss.is_cuda:
+        raise ValueError("dloss must be a float32 GPU tensor")
+    stride = 0 if dloss.numel() == 1 and N != 1 else 1
+    if stride == 1 and dloss.shape != (N,):
+        raise ValueError("dloss must have N elements or one")
+    dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
+    need = lib().cce_backward_workspace_bytes(N, V, D, dt)
+    ws = workspace(need, dev) if ws is None else ws
+    _check("cce_backward_shard", lib().cce_backward_shard(
+        _ptr(dloss), stride, _ptr(E), _ptr(C_shard), _ptr(targets), _ptr(lse), N, V, D, dt,
+        ignore_index, int(vocab_offset), float(filter_eps), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
+        ws.numel() * ws.element_size(), _ptr(skip_stats), _stream(stream)))
+    return dE, dC
 
 
 def timing_begin(kinds=KERNEL_KINDS, max_launches: int = 100000) -> None:

@@ -156,7 +156,7 @@ bool k_tail(int64_t D) {
 template <typename T>
 cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, int64_t V,
                         int64_t D, int64_t ii, float* loss, float* lse, void* ws, int32_t* err,
-                        hipStream_t st) {
+                        hipStream_t st, int64_t voff = 0, float* zt = nullptr) {
   const int64_t n_split = plan_splits(N, V);
   const int64_t n_tb = ceil_div(N, kTile), n_vt = ceil_div(V, kTile);
   const int64_t items = n_tb * n_split;
@@ -173,15 +173,16 @@ cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, i
   if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   TimedLaunch tl(CCE_KERNEL_FWD_FINISH, st);
   hipLaunchKernelGGL(k_fwd_finish<T>, dim3((unsigned)ceil_div(N, 4)), dim3(kFinishThreads), 0, st, E,
-                     C, tgt, (int)N, (int)V, (int)D, (int)n_split, part, ii, loss, lse, err);
+                     C, tgt, (int)N, (int)V, (int)D, (int)n_split, part, ii, loss, lse, err, voff,
+                     zt);
   return launch_status();
 }
 
 template <typename T>
 cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const T* C,
                          const int64_t* tgt, const float* lse, int64_t N, int64_t V, int64_t D,
-                         int64_t ii, float eps, void* dE, void* dC, cce_dtype gdt, void* ws,
-                         int64_t* skip_stats, hipStream_t st, cce_dtype dt) {
+                         int64_t ii, int64_t voff, float eps, void* dE, void* dC, cce_dtype gdt,
+                         void* ws, int64_t* skip_stats, hipStream_t st, cce_dtype dt) {
   const BwdLayout L = bwd_layout(N, V, D, dt);
   // dE accumulates over the chunks in fp32: in place, or in the workspace for bf16 output
   float* dE_acc = gdt == CCE_F32 ? (float*)dE : (float*)((char*)ws + L.acc_offset);
@@ -206,7 +207,7 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
     A.ldg = L.vc;
     A.flags = (uint8_t*)ws + 2 * L.g_bytes + buf * L.flag_bytes;
     A.fstride = (int)L.fstride;
-    A.eps = eps; A.ignore_index = ii;
+    A.eps = eps; A.ignore_index = ii; A.voff = voff;
     A.skip_count = (unsigned long long*)skip_stats;
     A.dE = dE_acc; A.dC = dC; A.dc_bf16 = gdt == CCE_BF16 ? 1 : 0;
     A.accumulate = c > 0 ? 1 : 0;
@@ -305,16 +306,23 @@ cce_status cce_forward(const void* E, const void* C, const int64_t* targets, int
                              loss, lse, ws, err_flag, st);
 }
 
-cce_status cce_backward(const float* dloss, int64_t dloss_stride, const void* E, const void* C,
-                        const int64_t* targets, const float* lse, int64_t N, int64_t V,
-                        int64_t D, cce_dtype dt, int64_t ignore_index, float filter_eps,
-                        void* dE, void* dC, cce_dtype grad_dtype, void* ws, size_t ws_bytes,
-                        int64_t* skip_stats, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// cce_backward and cce_backward_shard: vocabulary rows [voff, voff + V) in C.
+cce_status backward_entry(const float* dloss, int64_t dloss_stride, const void* E,
+                          const void* C, const int64_t* targets, const float* lse, int64_t N,
+                          int64_t V, int64_t D, cce_dtype dt, int64_t ignore_index,
+                          int64_t voff, float filter_eps, void* dE, void* dC,
+                          cce_dtype grad_dtype, void* ws, size_t ws_bytes, int64_t* skip_stats,
+                          void* stream) {
   if (!sizes_ok(N, V, D, dt)) return CCE_ERR_INVALID_ARGUMENT;
   if (!sizes_supported(N, V, D)) return CCE_ERR_UNSUPPORTED;
   if (!std::isfinite(filter_eps) || filter_eps < 0.f) return CCE_ERR_INVALID_ARGUMENT;
   if (dloss_stride != 0 && dloss_stride != 1) return CCE_ERR_INVALID_ARGUMENT;
   if (grad_dtype != CCE_F32 && grad_dtype != CCE_BF16) return CCE_ERR_INVALID_ARGUMENT;
+  if (voff < 0) return CCE_ERR_INVALID_ARGUMENT;
   if (N == 0) {
     // nothing to reduce: dC is still defined (all zero) and so are the statistics
     if (!dC) return CCE_ERR_INVALID_ARGUMENT;
@@ -335,11 +343,71 @@ cce_status cce_backward(const float* dloss, int64_t dloss_stride, const void* E,
   hipStream_t st = (hipStream_t)stream;
   if (dt == CCE_BF16)
     return backward_impl<__bf16>(dloss, dloss_stride, (const __bf16*)E, (const __bf16*)C,
-                                 targets, lse, N, V, D, ignore_index, filter_eps, dE, dC,
+                                 targets, lse, N, V, D, ignore_index, voff, filter_eps, dE, dC,
                                  grad_dtype, ws, skip_stats, st, dt);
   return backward_impl<float>(dloss, dloss_stride, (const float*)E, (const float*)C, targets,
-                              lse, N, V, D, ignore_index, filter_eps, dE, dC, grad_dtype, ws,
-                              skip_stats, st, dt);
+                              lse, N, V, D, ignore_index, voff, filter_eps, dE, dC, grad_dtype,
+                              ws, skip_stats, st, dt);
+}
+
+}  // namespace
+
+extern "C" {
+
+cce_status cce_backward(const float* dloss, int64_t dloss_stride, const void* E, const void* C,
+                        const int64_t* targets, const float* lse, int64_t N, int64_t V,
+                        int64_t D, cce_dtype dt, int64_t ignore_index, float filter_eps,
+                        void* dE, void* dC, cce_dtype grad_dtype, void* ws, size_t ws_bytes,
+                        int64_t* skip_stats, void* stream) {
+  return backward_entry(dloss, dloss_stride, E, C, targets, lse, N, V, D, dt, ignore_index, 0,
+                        filter_eps, dE, dC, grad_dtype, ws, ws_bytes, skip_stats, stream);
+}
+
+cce_status cce_backward_shard(const float* dloss, int64_t dloss_stride, const void* E,
+                              const void* C, const int64_t* targets, const float* lse,
+                              int64_t N, int64_t V, int64_t D, cce_dtype dt,
+                              int64_t ignore_index, int64_t vocab_offset, float filter_eps,
+                              void* dE, void* dC, cce_dtype grad_dtype, void* ws,
+                              size_t ws_bytes, int64_t* skip_stats, void* stream) {
+  return backward_entry(dloss, dloss_stride, E, C, targets, lse, N, V, D, dt, ignore_index,
+                        vocab_offset, filter_eps, dE, dC, grad_dtype, ws, ws_bytes, skip_stats,
+                        stream);
+}
+
+cce_status cce_forward_shard(const void* E, const void* C, const int64_t* targets, int64_t N,
+                             int64_t V, int64_t D, cce_dtype dt, int64_t ignore_index,
+                             int64_t vocab_offset, float* lse_shard, float* target_logit,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (!sizes_ok(N, V, D, dt)) return CCE_ERR_INVALID_ARGUMENT;
+  if (!sizes_supported(N, V, D)) return CCE_ERR_UNSUPPORTED;
+  if (vocab_offset < 0) return CCE_ERR_INVALID_ARGUMENT;
+  if (N == 0) return CCE_OK;
+  if (!E || !C || !targets || !lse_shard || !target_logit || !ws)
+    return CCE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < fwd_bytes(N, V)) return CCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = (hipStream_t)stream;
+  if (dt == CCE_BF16)
+    return forward_impl<__bf16>((const __bf16*)E, (const __bf16*)C, targets, N, V, D,
+                                ignore_index, nullptr, lse_shard, ws, nullptr, st, vocab_offset,
+                                target_logit);
+  return forward_impl<float>((const float*)E, (const float*)C, targets, N, V, D, ignore_index,
+                             nullptr, lse_shard, ws, nullptr, st, vocab_offset, target_logit);
+}
+
+cce_status cce_merge_shards(const float* lse_shards, const float* target_logits,
+                            int64_t n_shards, int64_t N, const int64_t* targets,
+                            int64_t ignore_index, int64_t V_total, float* loss, float* lse,
+                            int32_t* err_flag, void* stream) {
+  if (N < 0 || n_shards < 1 || n_shards > 65536 || V_total < 1 || N > kMaxRows)
+    return CCE_ERR_INVALID_ARGUMENT;
+  if (N == 0) return CCE_OK;
+  if (!lse_shards || !target_logits || !targets || !loss || !lse) return CCE_ERR_INVALID_ARGUMENT;
+  hipStream_t st = (hipStream_t)stream;
+  TimedLaunch tl(CCE_KERNEL_FWD_FINISH, st);
+  hipLaunchKernelGGL(k_merge_shards, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st,
+                     lse_shards, target_logits, (int)n_shards, (int)N, targets, ignore_index,
+                     V_total, loss, lse, err_flag);
+  return launch_status();
 }
 
 cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, int64_t N,

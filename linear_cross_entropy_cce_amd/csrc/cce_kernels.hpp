@@ -219,11 +219,15 @@ __device__ __forceinline__ float wave_max(float v) {
 // ------------------------------------------------------------------------------------------
 constexpr int kFinishThreads = 256;   // 4 tokens per workgroup, one wave each
 
+// Shard mode (zt != nullptr): C holds rows [voff, voff + V) of a larger vocabulary; the kernel
+// writes the LSE over those rows and zt[n] = the target logit when the target falls in them
+// (else 0), and no loss: the shards' results are merged by k_merge_shards.
 template <typename T>
 __global__ __launch_bounds__(kFinishThreads) void k_fwd_finish(
     const T* __restrict__ E, const T* __restrict__ C, const int64_t* __restrict__ tgt, int N,
     int V, int D, int n_split, const float2* __restrict__ part, int64_t ignore_index,
-    float* __restrict__ loss, float* __restrict__ lse, int32_t* __restrict__ err) {
+    float* __restrict__ loss, float* __restrict__ lse, int32_t* __restrict__ err, int64_t voff,
+    float* __restrict__ zt) {
   const int lane = threadIdx.x & 63;
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
@@ -240,11 +244,13 @@ __global__ __launch_bounds__(kFinishThreads) void k_fwd_finish(
   const float l = (mu + log2f(sum)) * kLn2;
   const int64_t t = tgt[n];
   const bool ignored = t == ignore_index;
-  const bool bad = !ignored && (t < 0 || t >= V);
+  const int64_t tl = t - voff;                     // row of the target within C
+  const bool here = !ignored && tl >= 0 && tl < V;
+  const bool bad = !ignored && !here && !zt;       // outside [0, V) is an error when unsharded
   float z = 0.f;
-  if (!ignored && !bad) {
+  if (here) {
     const T* e = E + (int64_t)n * D;
-    const T* c = C + t * (int64_t)D;
+    const T* c = C + tl * (int64_t)D;
     for (int d = lane * 4; d < D; d += 256) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) z += (float)e[d + i] * (float)c[d + i];
@@ -253,9 +259,39 @@ __global__ __launch_bounds__(kFinishThreads) void k_fwd_finish(
   }
   if (lane == 0) {
     lse[n] = l;
-    loss[n] = ignored ? 0.f : (bad ? __builtin_nanf("") : l - z);
-    if (bad && err) *err = 1;
+    if (zt) {
+      zt[n] = here ? z : 0.f;
+    } else {
+      loss[n] = ignored ? 0.f : (bad ? __builtin_nanf("") : l - z);
+      if (bad && err) *err = 1;
+    }
   }
+}
+
+// Merge of S vocabulary shards (k_fwd_finish in shard mode): lse = log sum_s exp lse_s, the
+// target logit is the one shard's contribution (the others wrote 0), loss = lse - z_t (0 for
+// ignored rows; NaN and *err = 1 for a target outside [0, V_total)).  One thread per token.
+__global__ void k_merge_shards(const float* __restrict__ lse_s, const float* __restrict__ zt_s,
+                               int S, int N, const int64_t* __restrict__ tgt,
+                               int64_t ignore_index, int64_t v_total, float* __restrict__ loss,
+                               float* __restrict__ lse, int32_t* __restrict__ err) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float m = -INFINITY;
+  for (int s = 0; s < S; ++s) m = fmaxf(m, lse_s[(int64_t)s * N + n]);
+  const float mu = m == -INFINITY ? 0.f : m;
+  float sum = 0.f, z = 0.f;
+  for (int s = 0; s < S; ++s) {
+    sum += exp2_fast((lse_s[(int64_t)s * N + n] - mu) * kLog2e);
+    z += zt_s[(int64_t)s * N + n];
+  }
+  const float l = mu + log2f(sum) * kLn2;
+  const int64_t t = tgt[n];
+  const bool ignored = t == ignore_index;
+  const bool bad = !ignored && (t < 0 || t >= v_total);
+  lse[n] = l;
+  loss[n] = ignored ? 0.f : (bad ? __builtin_nanf("") : l - z);
+  if (bad && err) *err = 1;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -282,6 +318,7 @@ struct BwdArgs {
   int fstride;
   float eps;
   int64_t ignore_index;
+  int64_t voff;               // vocabulary index of C's row 0 (a shard of a larger vocabulary)
   unsigned long long* skip_count;
   float* dE;                  // [N, D] fp32 accumulator of dE over the chunks
   void* dC;                   // [V, D] in the gradient dtype
@@ -348,7 +385,8 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
       ok = t != ignore_index;
       w = dloss[(int64_t)n * dstride];
       l2 = lse[n] * kLog2e;
-      const int64_t tl = t - (int64_t)v0 - vl0 - kWaveM * wm;  // target row within the wave's rows
+      // target row within the wave's rows
+      const int64_t tl = t - A.voff - (int64_t)v0 - vl0 - kWaveM * wm;
       tr = (ok && tl >= 0 && tl < 128) ? (int)tl : -1;
     }
     valid[ni] = ok;
