@@ -96,9 +96,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
     // valid K chunks from k0 (<= 0 on padding stages: all zeros)
     const int kc = KT ? (D - k0) / Traits<T>::kEpc : Geo<KB>::kChunks;
     const uint32_t soff = (uint32_t)k0 * sizeof(T);
-    const __amdgpu_buffer_rsrc_t rsC = kmajor_rsrc(c_cur + (nx ? (int64_t)kTile * D : 0),
+    const Rsrc rsC = kmajor_rsrc(c_cur + (nx ? (int64_t)kTile * D : 0),
                                                    live ? V - v_cur - (nx ? kTile : 0) : 0, ldb);
-    const __amdgpu_buffer_rsrc_t rsE =
+    const Rsrc rsE =
         kmajor_rsrc(E + (int64_t)tok0 * D, live ? N - tok0 : 0, ldb);
     return stage_issue<KB>(
         [=, &off](char* l, int q0, int q1) { kmajor_issue<KB>(rsC, off, soff, kc, l, wave, lane, q0, q1); },
@@ -361,8 +361,8 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
   kmajor_offsets<KB>(off, ldb, wave, lane);
   auto issue = [&](int it) {
     const bool live = it < n_k;   // past the end of the stream: zeros
-    const __amdgpu_buffer_rsrc_t rsC = kmajor_rsrc(Cc + (int64_t)vl0 * D, live ? vc - vl0 : 0, ldb);
-    const __amdgpu_buffer_rsrc_t rsE = kmajor_rsrc(E + (int64_t)tok0 * D, live ? N - tok0 : 0, ldb);
+    const Rsrc rsC = kmajor_rsrc(Cc + (int64_t)vl0 * D, live ? vc - vl0 : 0, ldb);
+    const Rsrc rsE = kmajor_rsrc(E + (int64_t)tok0 * D, live ? N - tok0 : 0, ldb);
     const int k0 = it * KS;
     const int kc = KT ? (D - k0) / Traits<T>::kEpc : Geo<KB>::kChunks;
     const uint32_t soff = (uint32_t)k0 * sizeof(T);
@@ -645,8 +645,8 @@ __device__ __forceinline__ void tile_bwd_de(const BwdArgs<T>& A, int lin, const 
     const int e = __builtin_amdgcn_readfirstlane(sList[live ? i : 0]);
     const int k0 = (e >> 4) * KS;
     const bool zero = (e >> (wave >> 1)) & 1;  // wave w loads token rows 32 w .. 32 w + 31
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(gt, (zero || !live) ? 0 : g_rec);
-    const __amdgpu_buffer_rsrc_t rb = mn_rsrc<T, KB>(Cc + (int64_t)k0 * D + d0,
+    const Rsrc ra = make_rsrc(gt, (zero || !live) ? 0 : g_rec);
+    const Rsrc rb = mn_rsrc<T, KB>(Cc + (int64_t)k0 * D + d0,
                                                      live ? vc - k0 : 0, ldb, d0 * (int)sizeof(T));
     const uint32_t soff = (uint32_t)k0 * sizeof(T);
     return stage_issue<KB>(
@@ -704,9 +704,9 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
       const int e = __builtin_amdgcn_readfirstlane(sList[live ? i : 0]);
       const int k0 = (sbase + (e >> 4)) * KS;
       const uint32_t zc = (uint32_t)(e & 15);
-      const __amdgpu_buffer_rsrc_t ra = mn_rsrc<T, KB>(
+      const Rsrc ra = mn_rsrc<T, KB>(
           G + (int64_t)k0 * ldg + vl0, live ? n_pad - k0 : 0, ldgb, vl0 * (int)sizeof(T));
-      const __amdgpu_buffer_rsrc_t rb = mn_rsrc<T, KB>(E + (int64_t)k0 * D + d0,
+      const Rsrc rb = mn_rsrc<T, KB>(E + (int64_t)k0 * D + d0,
                                                        live ? N - k0 : 0, ldb, d0 * (int)sizeof(T));
       return stage_issue<KB>(
           [=, &offA](char* l, int q0, int q1) { mn_issue<T, KB>(ra, offA, zc, l, wave, lane, q0, q1); },

@@ -29,7 +29,8 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kWaves = 8;
@@ -79,20 +80,33 @@ __device__ __forceinline__ void wait_vmcnt() {
 constexpr uint32_t kOob = 0x80000000u;         // offset answered with zeros
 constexpr int kRecords = 0x7FFFFFF0;           // descriptor range
 
-// Base and range are workgroup-uniform; readfirstlane states it, so the descriptor always
-// lives in scalar registers (never a per-lane "waterfall" loop over the loads).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int records) {
+// Buffer descriptor (V#) of a raw buffer: base address (48 bits, stride 0), byte range, and the
+// same format word as the compiler's buffer-resource builtin.  Base and range are
+// workgroup-uniform; readfirstlane states it, so the descriptor always lives in scalar
+// registers.
+typedef i32x4_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* p, int records) {
   const uint64_t a = (uint64_t)p;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  void* const pu = (void*)(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, __builtin_amdgcn_readfirstlane(records),
-                                           0x00020000);
+  Rsrc w;
+  w.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  w.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  w.z = __builtin_amdgcn_readfirstlane(records);
+  w.w = 0x00020000;
+  return w;
 }
 
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
-                                           uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+// One direct-to-LDS load: 64 lanes x 16 bytes from rsrc at voff + soff into LDS at lds (+ 16
+// bytes per lane).  Written as inline asm: the compiler then does not know that the
+// instruction writes LDS, so it adds no wait for it before later LDS reads of other buffers
+// (it cannot tell the transposing reads apart from the buffer being filled).  The pipeline
+// waits for these loads itself (wait_stages before the barrier of the stage that reads them).
+// No register receives data, so no register can be reused while the load is in flight.
+__device__ __forceinline__ void lds_load16(Rsrc rs, char* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t la = (uint32_t)(uintptr_t)(lds_char_t*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((int)la)), "v"(voff), "s"(rs), "s"(soff)
+               : "memory", "m0");
 }
 
 // Stage geometry.  KB = bytes of K per K-major operand row per stage (128 or 64): one
@@ -137,7 +151,7 @@ __device__ __forceinline__ void kmajor_offsets(uint32_t (&off)[Geo<KB>::kIssue],
 // rows of the operand from there: its range ends with the tile's last valid row, so later
 // rows load as zeros.  Stages step through K with the scalar offset of the loads, which
 // leaves the row test unchanged (a chunk never reaches past its own row).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t kmajor_rsrc(const void* origin, int rows_left,
+__device__ __forceinline__ Rsrc kmajor_rsrc(const void* origin, int rows_left,
                                                               int ld_bytes) {
   const int rows = rows_left < 0 ? 0 : (rows_left > kTile ? kTile : rows_left);
   return make_rsrc(origin, rows * ld_bytes);
@@ -146,7 +160,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kmajor_rsrc(const void* origin
 // Instructions [q0, q1) of this wave's share of a stage at byte offset soff along K.
 // k_chunks = valid 16-byte K chunks left from the stage's K origin (>= chunks per row: full).
 template <int KB>
-__device__ __forceinline__ void kmajor_issue(__amdgpu_buffer_rsrc_t rs,
+__device__ __forceinline__ void kmajor_issue(Rsrc rs,
                                              const uint32_t (&off)[Geo<KB>::kIssue],
                                              uint32_t soff, int k_chunks, char* lds, int wave,
                                              int lane, int q0 = 0, int q1 = Geo<KB>::kIssue) {
@@ -191,7 +205,7 @@ __device__ __forceinline__ void mn_offsets(uint32_t (&off)[Geo<KB>::kIssue], int
 // rows_left rows of the operand from k0 and col0 at byte col0_bytes of its row: the range ends
 // with the stage's last valid row.
 template <typename T, int KB>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t mn_rsrc(const void* origin, int rows_left,
+__device__ __forceinline__ Rsrc mn_rsrc(const void* origin, int rows_left,
                                                           int ld_bytes, int col0_bytes) {
   constexpr int R = KB / (int)sizeof(T);
   const int rows = rows_left < 0 ? 0 : (rows_left > R ? R : rows_left);
@@ -201,7 +215,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mn_rsrc(const void* origin, in
 
 // Instructions [q0, q1).  zero_cols bit b = load zeros for columns 64 b .. 64 b + 63.
 template <typename T, int KB>
-__device__ __forceinline__ void mn_issue(__amdgpu_buffer_rsrc_t rs,
+__device__ __forceinline__ void mn_issue(Rsrc rs,
                                          const uint32_t (&off)[Geo<KB>::kIssue],
                                          uint32_t zero_cols, char* lds, int wave, int lane,
                                          int q0 = 0, int q1 = Geo<KB>::kIssue) {
@@ -313,20 +327,14 @@ __device__ __forceinline__ void pin(f32x16_t& acc) { asm volatile("" : "+v"(acc)
 // One stage of MFMAs for this wave: KB / 32 k-groups x 4 x 2 blocks.  While the 8 MFMAs of the
 // first k-group run, part.one(j) issues the j-th load of a later stage, one after each MFMA,
 // so the address units never stall the MFMA issue and the loads get the rest of the stage to
-// land.  K-major fragments of group g + 1 are read while group g runs.  Transposing LDS reads
-// carry no alias information for the compiler, which would make each of them wait for every
-// direct-to-LDS load in flight, so the fragments of an MN-major bf16 operand are all read, for
-// every group of the stage, before the loads are issued.  Scheduling barriers and the
-// accumulator pins keep this order.
+// land.  The fragments of group g + 1 are read while group g runs.  Scheduling barriers and
+// the accumulator pins keep this order.
 template <typename T, int KB, bool AK, bool BK, typename Part = NoIssue>
 __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Acc& acc, int wm,
                                               int wn, int lane, const Part& part = Part()) {
   typedef typename Traits<T>::frag_t F;
   constexpr int G = Geo<KB>::kGroups;
-  constexpr bool kEA = sizeof(T) == 2 && !AK;   // operand read for the whole stage up front
-  constexpr bool kEB = sizeof(T) == 2 && !BK;
-  constexpr int SA = kEA ? G : 2, SB = kEB ? G : 2;
-  F a[SA][kMB], b[SB][kNB];
+  F a[2][kMB], b[2][kNB];
   auto read_a = [&](int slot, int g) {
 #pragma unroll
     for (int i = 0; i < kMB; ++i) a[slot][i] = frag<T, KB, AK>(As, kWaveM * wm + 32 * i, g, lane);
@@ -337,18 +345,13 @@ __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Ac
   };
   read_a(0, 0);
   read_b(0, 0);
-#pragma unroll
-  for (int g = 1; g < G; ++g) {
-    if (kEA) read_a(g, g);
-    if (kEB) read_b(g, g);
-  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int ca = kEA ? g : (g & 1), cb = kEB ? g : (g & 1);
+    const int ca = g & 1, cb = g & 1;
     if (g + 1 < G) {
-      if (!kEA) read_a((g + 1) & 1, g + 1);
-      if (!kEB) read_b((g + 1) & 1, g + 1);
+      read_a((g + 1) & 1, g + 1);
+      read_b((g + 1) & 1, g + 1);
     }
 #pragma unroll
     for (int mi = 0; mi < kMB; ++mi)
