@@ -402,11 +402,6 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
   // 64 x 64 block the largest p (independent maxima, no serial chains)
   const bool filter = eps > 0.f;
   const bool full = vl0 + kTile <= vc;
-  float pmax[2][kNB];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int ni = 0; ni < kNB; ++ni) pmax[a][ni] = 0.f;
   if (!full) {
     // last tile of the chunk: rows at or past vc get p = 0
     const int lim = vc - vl0 - kWaveM * wm - acc_row_l(lane);
@@ -423,71 +418,68 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
   int tcmp[kNB];
 #pragma unroll
   for (int ni = 0; ni < kNB; ++ni) tcmp[ni] = trow[ni] - acc_row_l(lane);
-#pragma unroll
-  for (int ni = 0; ni < kNB; ++ni)
-#pragma unroll
-    for (int mi = 0; mi < kMB; ++mi)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(__builtin_fmaf(acc[mi][ni][r], kLog2e, -lse2[ni]));
-        pmax[mi >> 1][ni] = fmaxf(pmax[mi >> 1][ni], p);
-        acc[mi][ni][r] =
-            __builtin_fmaf(coef[ni], p, acc_row_c(mi, r) == tcmp[ni] ? -coef[ni] : 0.f);
-      }
-  // the wave's 64 token columns are one filter block wide; its 128 vocabulary rows two blocks
-  bool sig[2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    bool any = false;
-#pragma unroll
-    for (int ni = 0; ni < kNB; ++ni) {
-      const bool has_t = trow[ni] >= 64 * a && trow[ni] < 64 * a + 64;
-      any |= valid[ni] && (pmax[a][ni] >= eps || has_t);
-    }
-    sig[a] = any;
-  }
 
-  // block decisions (wave-wide), flags, statistics
+  // The wave's 64 token columns are one filter block wide and its 128 vocabulary rows two
+  // blocks (a = 0, 1: register blocks mi = 2a, 2a + 1).  Each block is finished in turn --
+  // G, the wave-wide keep decision, its flag, its store -- so the stores of the first block
+  // are in flight while the second is computed.
   int n_skipped = 0;
-  bool keep[2];
   const int nblk = tok0 + kWaveN * wn;          // token start of the wave's block
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    const int vblk = vl0 + kWaveM * wm + 64 * a;  // chunk-local vocab start of the block
-    const bool in_range = vblk < vc && nblk < N;
-    const bool any = __ballot(sig[a]) != 0ull;
-    const bool k = in_range && (!filter || any);
-    keep[a] = k;
-    if (in_range && !k) ++n_skipped;
-    if (lane == 0) flags[(int64_t)(nblk >> 6) * fstride + (vblk >> 6)] = k ? 0 : 1;
-  }
-  if (skip_count && lane == 0 && n_skipped) atomicAdd(skip_count, (unsigned long long)n_skipped);
-
-  // store the kept blocks: 4 consecutive vocab rows of one token per lane and register group
+    float pmax[kNB];
 #pragma unroll
-  for (int mi = 0; mi < kMB; ++mi)
+    for (int ni = 0; ni < kNB; ++ni) pmax[ni] = 0.f;
+#pragma unroll
+    for (int ni = 0; ni < kNB; ++ni)
+#pragma unroll
+      for (int mi = 2 * a; mi < 2 * a + 2; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_fast(__builtin_fmaf(acc[mi][ni][r], kLog2e, -lse2[ni]));
+          pmax[ni] = fmaxf(pmax[ni], p);
+          acc[mi][ni][r] =
+              __builtin_fmaf(coef[ni], p, acc_row_c(mi, r) == tcmp[ni] ? -coef[ni] : 0.f);
+        }
+    bool sig = false;
 #pragma unroll
     for (int ni = 0; ni < kNB; ++ni) {
-      if (!keep[mi >> 1]) continue;
-      const int n = tok0 + kWaveN * wn + 32 * ni + (lane & 31);
+      const bool has_t = trow[ni] >= 64 * a && trow[ni] < 64 * a + 64;
+      sig |= valid[ni] && (pmax[ni] >= eps || has_t);
+    }
+    // block decision (wave-wide), flag, statistics
+    const int vblk = vl0 + kWaveM * wm + 64 * a;  // chunk-local vocab start of the block
+    const bool in_range = vblk < vc && nblk < N;
+    const bool keep = in_range && (!filter || __ballot(sig) != 0ull);
+    if (in_range && !keep) ++n_skipped;
+    if (lane == 0) flags[(int64_t)(nblk >> 6) * fstride + (vblk >> 6)] = keep ? 0 : 1;
+    if (!keep) continue;
+    // store: 4 consecutive vocab rows of one token per lane and register group
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int vloc = vl0 + kWaveM * wm + 32 * mi + 8 * rq + 4 * (lane >> 5);
-        T* dst = G + (int64_t)n * ldg + vloc;
-        if constexpr (sizeof(T) == 2) {
-          typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
-          bf16x4_t v;
+    for (int mi = 2 * a; mi < 2 * a + 2; ++mi)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (__bf16)acc[mi][ni][4 * rq + i];
-          *(bf16x4_t*)dst = v;
-        } else {
-          f32x4_t v;
+      for (int ni = 0; ni < kNB; ++ni) {
+        const int n = tok0 + kWaveN * wn + 32 * ni + (lane & 31);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[mi][ni][4 * rq + i];
-          *(f32x4_t*)dst = v;
+        for (int rq = 0; rq < 4; ++rq) {
+          const int vloc = vl0 + kWaveM * wm + 32 * mi + 8 * rq + 4 * (lane >> 5);
+          T* dst = G + (int64_t)n * ldg + vloc;
+          if constexpr (sizeof(T) == 2) {
+            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+            bf16x4_t v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (__bf16)acc[mi][ni][4 * rq + i];
+            *(bf16x4_t*)dst = v;
+          } else {
+            f32x4_t v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc[mi][ni][4 * rq + i];
+            *(f32x4_t*)dst = v;
+          }
         }
       }
-    }
+  }
+  if (skip_count && lane == 0 && n_skipped) atomicAdd(skip_count, (unsigned long long)n_skipped);
 }
 
 // Writes this wave's 128 x 64 accumulators to a row-major bf16 matrix out[rows][ld] at
