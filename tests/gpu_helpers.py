@@ -71,7 +71,12 @@ def borderline_blocks(E, C, t, eps, bn=64, bv=64, rel_band=1e-3):
     return count
 
 
-def check_against_oracle(d, dtype, w, eps, name, grad_tol=GRAD_TOL, loss_tol=LOSS_TOL):
+def check_against_oracle(d, dtype, w, eps, name, grad_tol=GRAD_TOL, loss_tol=LOSS_TOL,
+                         vs_unfiltered=True):
+    """Element-by-element comparison with the oracle's result for the same filter threshold;
+    with vs_unfiltered, a filtered result must also stay within tolerance of the unfiltered
+    oracle (the approximation bound the benchmarks' threshold is held to on realistic logit
+    spreads; arbitrary spreads and thresholds need not meet it)."""
     log(f"[{name}] N={d['E'].shape[0]} D={d['E'].shape[1]} V={d['C'].shape[0]} {dtype} eps={eps}")
     g = gpu_run(d, dtype, w, eps)
     E, C, t = d["E"], d["C"], d["targets"]
@@ -86,7 +91,7 @@ def check_against_oracle(d, dtype, w, eps, name, grad_tol=GRAD_TOL, loss_tol=LOS
     assert g["total"] == tot
     border = borderline_blocks(E, C, t, eps)
     assert abs(g["skipped"] - sk) <= border, (g["skipped"], sk, border)
-    if eps > 0:   # the filtered result is also within tolerance of the unfiltered oracle
+    if eps > 0 and vs_unfiltered:   # also within tolerance of the unfiltered oracle
         dE0, dC0, _ = oracle.backward(E, C, t, w, II)
         assert rel(g["dE"], dE0) <= GRAD_TOL and rel(g["dC"], dC0) <= GRAD_TOL
     log(f"[{name}] ok: loss {np.abs(g['loss'] - loss).max():.2e} dE {rel(g['dE'], dE):.2e} "

@@ -207,3 +207,29 @@ def test_empty_batch_bf16_gradients():
                               grad_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert dE.numel() == 0 and float(dC.float().abs().max()) == 0.0
+
+
+def _random_cases(n, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dt = "bf16" if rng.random() < 0.7 else "f32"
+        step = 8 if dt == "bf16" else 4
+        N = int(rng.integers(1, 700))
+        D = int(rng.integers(1, 41)) * step
+        V = int(rng.integers(1, 5000))
+        cs = float(rng.choice([1.0, 3.0, 8.0]))
+        z = None if rng.random() < 0.3 else float(rng.choice([1.0, 1.1, 1.3]))
+        ig = float(rng.choice([0.0, 0.1, 0.5]))
+        eps = float(rng.choice([0.0, EPS, 1e-3]))
+        cases.append((f"r{i}_{dt}_{N}x{D}x{V}", N, D, V, dt, cs, z, ig, eps, 500 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(12), ids=lambda c: c[0])
+def test_random_shapes(case):
+    """Seeded random shapes (ragged N, D and V, both dtypes, ignored rows, three thresholds)
+    against the oracle with the same threshold, element by element."""
+    name, N, D, V, dt, cs, z, ig, eps, seed = case
+    d = S.small_case(N, D, V, dt, seed, cs, z, ig)
+    check_against_oracle(d, dt, S.dloss_weights(seed, N), eps, name, vs_unfiltered=False)
