@@ -3,8 +3,9 @@
 // Host-side plan for the Cut Cross-Entropy abstract's method (taxoreview.com page
 // dblp:393/3562, sentences 4-6 and 9):
 //   forward : k_fwd_lse over (token tile x vocabulary range), then k_fwd_finish;
-//   backward: for each vocabulary chunk of Vc rows, k_bwd_g -> k_bwd_dc -> k_bwd_de on the
-//             caller's stream; only the chunk's G tiles (N x Vc) ever live in the workspace.
+//   backward: k_bwd_g for the first vocabulary chunk of Vc rows, then one k_bwd_fused per
+//             chunk c (dE and dC of c, G of c + 1), all on the caller's stream; only the G of
+//             two chunks (N x Vc each) ever lives in the workspace.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

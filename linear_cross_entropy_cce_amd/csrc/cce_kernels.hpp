@@ -8,12 +8,16 @@
 //
 //   k_fwd_lse     S = C_tile E_tile^T on MFMA, online (max, sum exp) per token over the
 //                 workgroup's vocabulary range, one partial per (range, token).
-//   k_fwd_finish  merge of the partials (no atomics), target logit by gather-dot, loss.
-//   k_bwd_g       recomputes S for a vocabulary chunk, forms G = dloss (softmax - onehot) in
-//                 registers, flags negligible 64 x 64 blocks, stores the rest of G (bf16).
-//   k_bwd_de      dE (+)= G C over the chunk, skipping flagged K stages.
-//   k_bwd_dc      dC_chunk = G^T E, skipping flagged K stages.
-//   k_mean, k_skip_init  small helpers for the mean-reduced call and the skip statistics.
+//   k_fwd_finish  merge of the partials (no atomics), target logit by gather-dot, loss; in
+//                 shard mode the LSE over a shard of the vocabulary and the target logit.
+//   k_merge_shards  merge of per-shard LSEs and target logits into loss and LSE.
+//   k_bwd_g       recomputes S for a vocabulary chunk (tile_bwd_g), forms
+//                 G = dloss (softmax - onehot) in registers, flags negligible 64 x 64 blocks,
+//                 stores the rest of G (bf16).
+//   k_bwd_fused   per chunk c: dE (+)= G_c C_c (tile_bwd_de) and dC_c = G_c^T E (tile_bwd_dc),
+//                 skipping flagged K stages, together with tile_bwd_g of chunk c + 1.
+//   k_f32_to_bf16, k_zero_f32, k_mean, k_skip_init  small helpers (bf16 gradient output,
+//                 empty batches, the mean-reduced call, the skip statistics).
 #pragma once
 
 #include "tile_engine.hpp"
