@@ -557,46 +557,99 @@ __device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, 
 // skipped within the stage (its operand chunk is loaded as zeros).
 //   rowwise: flags of stage s are flags[(fr0 + b) * fstride + s * KS / 64]   (dE: K = vocab)
 //   else   : flags of stage s are flags[(s * KS / 64) * fstride + fc0 + b]   (dC: K = tokens)
+// The list comes in three segments, each in stage order and padded to a multiple of NST with
+// all-zero stages (mask 15): stages whose live blocks are all in rows 0..127 (blocks 0, 1),
+// then stages with live blocks in both 128-row halves of the tile, then stages whose live
+// blocks are all in rows 128..255.  seg[k] = padded length of segment k.  wave_cnt: 6 x kWaves
+// ints of LDS.
 template <int KS, int NST>
-__device__ __forceinline__ int build_stage_list(const uint8_t* __restrict__ flags, int fstride,
-                                                int n_stages, bool rowwise, int fixed0,
-                                                int* list, int* wave_cnt) {
+__device__ __forceinline__ void build_stage_list(const uint8_t* __restrict__ flags, int fstride,
+                                                 int n_stages, bool rowwise, int fixed0,
+                                                 int* list, int* wave_cnt, int (&seg)[3]) {
   const int lane = threadIdx.x & 63, wave = wave_id();
-  int total = 0;
-  for (int base = 0; base < n_stages; base += kThreads) {
-    const int s = base + threadIdx.x;
-    uint32_t mask = 15u;
-    if (s < n_stages) {
-      const int fk = (s * KS) >> 6;
-      mask = 0u;
+  // segment of stage s: 0 only rows 0..127 live, 1 both halves, 2 only rows 128..255, -1 none
+  auto classify = [&](int s, uint32_t& mask) -> int {
+    mask = 15u;
+    if (s >= n_stages) return -1;
+    const int fk = (s * KS) >> 6;
+    mask = 0u;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint8_t f = rowwise ? flags[(int64_t)(fixed0 + b) * fstride + fk]
-                                  : flags[(int64_t)fk * fstride + fixed0 + b];
-        mask |= (f ? 1u : 0u) << b;
-      }
+    for (int b = 0; b < 4; ++b) {
+      const uint8_t f = rowwise ? flags[(int64_t)(fixed0 + b) * fstride + fk]
+                                : flags[(int64_t)fk * fstride + fixed0 + b];
+      mask |= (f ? 1u : 0u) << b;
     }
-    const bool active = s < n_stages && mask != 15u;
-    const unsigned long long bal = __ballot(active);
-    if (lane == 0) wave_cnt[wave] = __popcll(bal);
-    __syncthreads();
-    int off = total;
-    for (int w = 0; w < wave; ++w) off += wave_cnt[w];
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (active) list[off + before] = (s << 4) | (int)mask;
+    const bool lo = (mask & 3u) != 3u, hi = (mask >> 2) != 3u;
+    return lo && hi ? 1 : lo ? 0 : hi ? 2 : -1;
+  };
+  const unsigned long long below = (1ull << lane) - 1ull;
+  // stages [0, kThreads): one per thread, classified once; later stages only counted here
+  uint32_t mask0;
+  const int k0 = classify(threadIdx.x, mask0);
+  int rest[3] = {0, 0, 0};
+  for (int base = kThreads; base < n_stages; base += kThreads) {
+    uint32_t mask;
+    const int k = classify(base + threadIdx.x, mask);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) total += wave_cnt[w];
-    __syncthreads();
+    for (int j = 0; j < 3; ++j) rest[j] += __popcll(__ballot(k == j));
   }
-  // pad to a multiple of NST with all-zero stages (every block masked), so the pipeline runs
-  // whole rounds of stages
-  const int padded = (total + NST - 1) / NST * NST;
-  if (padded != total) {
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int c = __popcll(__ballot(k0 == j));
+    if (lane == 0) {
+      wave_cnt[j * kWaves + wave] = c;
+      wave_cnt[(3 + j) * kWaves + wave] = rest[j];
+    }
+  }
+  __syncthreads();
+  // segment j starts at `start`; its first-step entries go first, in wave order, then its later
+  // entries from pos[j]; pads fill its end
+  int pos[3], start = 0;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    int n0 = 0, nb = 0, nr = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = wave_cnt[j * kWaves + w];
+      n0 += c;
+      nb += w < wave ? c : 0;
+      nr += wave_cnt[(3 + j) * kWaves + w];
+    }
+    const unsigned long long bal = __ballot(k0 == j);
+    if (k0 == j) list[start + nb + __popcll(bal & below)] = ((int)threadIdx.x << 4) | (int)mask0;
+    seg[j] = (n0 + nr + NST - 1) / NST * NST;
+    // pads: all-zero stages (every block masked), so the pipeline runs whole rounds
     if (threadIdx.x == 0)
-      for (int i = total; i < padded; ++i) list[i] = 15;
-    __syncthreads();
+      for (int i = start + n0 + nr; i < start + seg[j]; ++i) list[i] = 15;
+    pos[j] = start + n0;
+    start += seg[j];
   }
-  return padded;
+  // later stages: each after the earlier ones of its segment
+  for (int base = kThreads; base < n_stages; base += kThreads) {
+    uint32_t mask;
+    const int k = classify(base + threadIdx.x, mask);
+    __syncthreads();   // the counts of the previous step have been read
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int c = __popcll(__ballot(k == j));
+      if (lane == 0) wave_cnt[j * kWaves + wave] = c;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      int off = pos[j], sum = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int c = wave_cnt[j * kWaves + w];
+        off += w < wave ? c : 0;
+        sum += c;
+      }
+      const unsigned long long bal = __ballot(k == j);
+      if (k == j) list[off + __popcll(bal & below)] = ((base + (int)threadIdx.x) << 4) | (int)mask;
+      pos[j] += sum;
+    }
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------------------------------
@@ -624,8 +677,9 @@ __device__ __forceinline__ void tile_bwd_de(const BwdArgs<T>& A, int lin, const 
   const int wm = wave_m(wave), wn = wave_n(wave);
   const int tok0 = tb * kTile, d0 = dt * kTile;
   const int n_stages = kv / KS;
-  const int n_act =
-      build_stage_list<KS, NST>(flags, fstride, n_stages, true, tb * 4, sList, sCnt);
+  int seg[3];
+  build_stage_list<KS, NST>(flags, fstride, n_stages, true, tb * 4, sList, sCnt, seg);
+  const int n_act = seg[0] + seg[1] + seg[2];
 
   Acc acc;
   zero_acc(acc);
@@ -651,10 +705,7 @@ __device__ __forceinline__ void tile_bwd_de(const BwdArgs<T>& A, int lin, const 
         },
         [=, &offB](char* l, int q0, int q1) { mn_issue<T, KB>(rb, offB, 0u, l, wave, lane, q0, q1); });
   };
-  if (n_act > 0) {
-    run_prologue<KB, NST>(n_act, issue, B);
-    run_stream<T, KB, NST, true, false>(0, n_act, n_act, issue, B, acc, wm, wn, lane);
-  }
+  run_segments<T, KB, NST, true, false>(seg, issue, B, acc, wm, wn, lane);
   store_tile(dE, D, tok0 + kWaveM * wm, N, d0 + kWaveN * wn, D, acc, lane, accumulate != 0);
 }
 
@@ -693,8 +744,10 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
   zero_acc(acc);
   for (int sbase = 0; sbase < n_stages; sbase += kPiece) {
     const int cnt = min(kPiece, n_stages - sbase);
-    const int n_act = build_stage_list<KS, NST>(flags + (int64_t)((sbase * KS) >> 6) * fstride,
-                                                fstride, cnt, false, vt * 4, sList, sCnt);
+    int seg[3];
+    build_stage_list<KS, NST>(flags + (int64_t)((sbase * KS) >> 6) * fstride, fstride, cnt,
+                              false, vt * 4, sList, sCnt, seg);
+    const int n_act = seg[0] + seg[1] + seg[2];
     auto issue = [&](int i) {
       const bool live = i < n_act;   // past the end of the list: zeros
       const int e = __builtin_amdgcn_readfirstlane(sList[live ? i : 0]);
@@ -708,10 +761,7 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
           [=, &offA](char* l, int q0, int q1) { mn_issue<T, KB>(ra, offA, zc, l, wave, lane, q0, q1); },
           [=, &offB](char* l, int q0, int q1) { mn_issue<T, KB>(rb, offB, 0u, l, wave, lane, q0, q1); });
     };
-    if (n_act > 0) {
-      run_prologue<KB, NST>(n_act, issue, B);
-      run_stream<T, KB, NST, false, false>(0, n_act, n_act, issue, B, acc, wm, wn, lane);
-    }
+    run_segments<T, KB, NST, false, false>(seg, issue, B, acc, wm, wn, lane);
     __syncthreads();
   }
   if (A.dc_bf16)
@@ -741,8 +791,8 @@ template <typename T, int KB, int NST, bool KT>
 __global__ __launch_bounds__(kThreads, 1) void k_bwd_fused(BwdArgs<T> A, BwdArgs<T> next,
                                                            int r_de, int r_dc) {
   CCE_STAGE_BUFFERS(KB, NST, B)
-  __shared__ int sList[kDcPiece + NST];
-  __shared__ int sCnt[kWaves];
+  __shared__ int sList[kDcPiece + 3 * NST];
+  __shared__ int sCnt[6 * kWaves];
   const int b = blockIdx.x;
   if (b < r_de) {
     tile_bwd_de<T, KB, NST>(A, xcd_remap(b, r_de), B, sList, sCnt);

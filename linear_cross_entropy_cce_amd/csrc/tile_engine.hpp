@@ -456,6 +456,24 @@ __device__ __forceinline__ void run_stream(int base, int n, int total, Issue&& i
   if (base + n >= total) wait_vmcnt<0>();
 }
 
+// The same pipeline for a wave that has no MFMAs in stages [base, base + n): it issues its share
+// of the loads and keeps the waits and barriers of the waves that compute.
+template <int KB, int NST, typename Issue>
+__device__ __forceinline__ void run_stream_idle(int base, int n, int total, Issue&& issue,
+                                                const Bufs<NST>& B) {
+  constexpr int P = NST - 1;
+  for (int g0 = base; g0 < base + n; g0 += NST) {
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+      wait_stages<KB, NST>(P - 1);
+      stage_barrier();
+      const auto st = issue(g0 + u + P);
+      st(B.a[(u + P) % NST], B.b[(u + P) % NST], 0, Geo<KB>::kIssue);
+    }
+  }
+  if (base + n >= total) wait_vmcnt<0>();
+}
+
 // Issues the first NST - 1 stages of a stream (fewer if the stream is shorter).
 template <int KB, int NST, typename Issue>
 __device__ __forceinline__ void run_prologue(int total, Issue&& issue, const Bufs<NST>& B) {
@@ -465,6 +483,26 @@ __device__ __forceinline__ void run_prologue(int total, Issue&& issue, const Buf
       const auto st = issue(u);
       st(B.a[u], B.b[u], 0, Geo<KB>::kIssue);
     }
+}
+
+// A stage list in three segments (lengths seg[0..2], multiples of NST): stages where only rows
+// 0..127 of the tile's A operand are live, stages where both halves are, stages where only
+// rows 128..255 are.  The waves of rows 0..127 (wm = 0) compute the first two segments, those
+// of rows 128..255 the last two: their rows of A are all zero in the other segment.  A wave
+// outside its range issues its loads and keeps the barriers, so its SIMD partner of the other
+// half runs alone.  Each wave runs one compute loop over one contiguous range.
+template <typename T, int KB, int NST, bool AK, bool BK, typename Issue>
+__device__ __forceinline__ void run_segments(const int (&seg)[3], Issue&& issue,
+                                             const Bufs<NST>& B, Acc& acc, int wm, int wn,
+                                             int lane) {
+  const int total = seg[0] + seg[1] + seg[2];
+  if (total == 0) return;
+  const int c0 = wm == 0 ? 0 : seg[0];
+  const int c1 = wm == 0 ? seg[0] + seg[1] : total;
+  run_prologue<KB, NST>(total, issue, B);
+  run_stream_idle<KB, NST>(0, c0, total, issue, B);
+  run_stream<T, KB, NST, AK, BK>(c0, c1 - c0, total, issue, B, acc, wm, wn, lane);
+  run_stream_idle<KB, NST>(c1, total - c1, total, issue, B);
 }
 
 __device__ __forceinline__ void zero_acc(Acc& acc) {

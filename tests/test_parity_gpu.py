@@ -233,3 +233,44 @@ def test_random_shapes(case):
     name, N, D, V, dt, cs, z, ig, eps, seed = case
     d = S.small_case(N, D, V, dt, seed, cs, z, ig)
     check_against_oracle(d, dt, S.dloss_weights(seed, N), eps, name, vs_unfiltered=False)
+
+
+def _half_live_case(N, V, D, dtype, seed):
+    """Inputs whose live 64 x 64 blocks follow a fixed pattern: token block b is "flat" (small
+    logits, every softmax entry near 1/V, live everywhere) when b % 8 == 0, else it leans on
+    vocabulary rows of its parity class g = (b // 2) % 2, where row v has class (v // 128) % 2:
+    blocks of the same class are live, the others are negligible.  Within a 256-row tile of
+    either product, many K stages have live blocks in only one 128-row half of the tile and
+    others in both; targets lie in the token's own class (or anywhere for flat tokens)."""
+    g = np.random.default_rng(seed)
+    tb = np.arange(N) // 64
+    flat = tb % 8 == 0
+    cls_n = (tb // 2) % 2
+    cls_v = (np.arange(V) // 128) % 2
+    E = 0.3 * g.standard_normal((N, D))
+    E[np.arange(N), cls_n] += np.where(flat, 0.0, 6.0)
+    E[flat] *= 0.1
+    C = 0.3 * g.standard_normal((V, D))
+    C[np.arange(V), cls_v] += 3.0
+    t = np.empty(N, np.int64)
+    for c in (0, 1):
+        rows = np.flatnonzero((cls_n == c) & ~flat)
+        t[rows] = g.choice(np.flatnonzero(cls_v == c), size=rows.size)
+    t[flat] = g.integers(0, V, size=int(flat.sum()))
+    t[g.random(N) < 0.05] = II
+    rnd = S.bf16_round if dtype == "bf16" else (lambda x: x)
+    return {"E": rnd(E.astype(np.float32)), "C": rnd(C.astype(np.float32)), "targets": t}
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 40000), ("f32", 20000)])
+def test_stages_with_one_live_half(dtype, N):
+    """Backward stages whose live blocks sit in one 128-row half of a tile (only that half's
+    waves multiply), mixed with stages live in both halves, and token counts whose stage lists
+    take several 512-entry steps to build: element-wise parity with the oracle, and exactly the
+    oracle's skipped blocks (no block is near the threshold)."""
+    V, D = 1000, 64
+    d = _half_live_case(N, V, D, dtype, 71)
+    g = check_against_oracle(d, dtype, S.dloss_weights(71, N), EPS, f"half_live_{dtype}")
+    _, _, (sk, tot) = oracle.backward(d["E"], d["C"], d["targets"],
+                                      S.dloss_weights(71, N), II, filter_eps=EPS)
+    assert g["skipped"] == sk and 0.3 * tot < sk < 0.6 * tot, (g["skipped"], sk, tot)
