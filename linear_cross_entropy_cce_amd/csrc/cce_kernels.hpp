@@ -435,16 +435,31 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
 #pragma unroll
     for (int ni = 0; ni < kNB; ++ni) pmax[ni] = 0.f;
 #pragma unroll
-    for (int ni = 0; ni < kNB; ++ni)
+    for (int ni = 0; ni < kNB; ++ni) {
+      // the one-hot term only where some column of the wave has its target in this block
+      // (a uniform branch; fma with a zero addend rounds like the general form)
+      const bool any_t = __ballot(trow[ni] >= 64 * a && trow[ni] < 64 * a + 64) != 0ull;
+      if (any_t) {
 #pragma unroll
-      for (int mi = 2 * a; mi < 2 * a + 2; ++mi)
+        for (int mi = 2 * a; mi < 2 * a + 2; ++mi)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(__builtin_fmaf(acc[mi][ni][r], kLog2e, -lse2[ni]));
-          pmax[ni] = fmaxf(pmax[ni], p);
-          acc[mi][ni][r] =
-              __builtin_fmaf(coef[ni], p, acc_row_c(mi, r) == tcmp[ni] ? -coef[ni] : 0.f);
-        }
+          for (int r = 0; r < 16; ++r) {
+            const float p = exp2_fast(__builtin_fmaf(acc[mi][ni][r], kLog2e, -lse2[ni]));
+            pmax[ni] = fmaxf(pmax[ni], p);
+            acc[mi][ni][r] =
+                __builtin_fmaf(coef[ni], p, acc_row_c(mi, r) == tcmp[ni] ? -coef[ni] : 0.f);
+          }
+      } else {
+#pragma unroll
+        for (int mi = 2 * a; mi < 2 * a + 2; ++mi)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = exp2_fast(__builtin_fmaf(acc[mi][ni][r], kLog2e, -lse2[ni]));
+            pmax[ni] = fmaxf(pmax[ni], p);
+            acc[mi][ni][r] = __builtin_fmaf(coef[ni], p, 0.f);
+          }
+      }
+    }
     bool sig = false;
 #pragma unroll
     for (int ni = 0; ni < kNB; ++ni) {
