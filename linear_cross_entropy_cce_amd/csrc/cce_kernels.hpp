@@ -519,35 +519,20 @@ __device__ __forceinline__ void store_tile_bf16(__bf16* __restrict__ out, int64_
       }
 }
 
-// Writes (or adds) this wave's 128 x 64 accumulators to a row-major fp32 matrix out[rows][ld]
-// at (row0, col0); rows >= row_lim and columns >= col_lim are dropped.  For each register a
-// half-wave writes 32 consecutive columns (128 bytes).  Adding uses the L2's float atomic add
-// without return, so no load latency is exposed; it stays deterministic because each element
-// receives one add per launch and launches are ordered on the stream.
-__device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, int row0,
-                                           int row_lim, int col0, int col_lim, Acc& acc,
-                                           int lane, bool add) {
-  const bool full = row0 + kWaveM <= row_lim && col0 + kWaveN <= col_lim;
-  if (full && !add) {
+// acc = in[rows, cols] of the wave's 128 x 64 part of a row-major fp32 matrix (zero outside the
+// limits): the running sum of a tile that this workgroup alone updates in the launch.
+__device__ __forceinline__ void load_tile(const float* __restrict__ in, int64_t ld, int row0,
+                                          int row_lim, int col0, int col_lim, Acc& acc,
+                                          int lane) {
+  if (row0 + kWaveM <= row_lim && col0 + kWaveN <= col_lim) {
 #pragma unroll
     for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
       for (int ni = 0; ni < kNB; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          out[(int64_t)(row0 + 32 * mi + acc_row(r, lane)) * ld + col0 + 32 * ni + (lane & 31)] =
-              acc[mi][ni][r];
-  } else if (full) {
-#pragma unroll
-    for (int mi = 0; mi < kMB; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < kNB; ++ni)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float* p =
-              out + (int64_t)(row0 + 32 * mi + acc_row(r, lane)) * ld + col0 + 32 * ni + (lane & 31);
-          atomicAddNoRet(p, acc[mi][ni][r]);
-        }
+          acc[mi][ni][r] =
+              in[(int64_t)(row0 + 32 * mi + acc_row(r, lane)) * ld + col0 + 32 * ni + (lane & 31)];
   } else {
 #pragma unroll
     for (int mi = 0; mi < kMB; ++mi)
@@ -556,13 +541,36 @@ __device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = row0 + 32 * mi + acc_row(r, lane), col = col0 + 32 * ni + (lane & 31);
-          if (row < row_lim && col < col_lim) {
-            float* p = out + (int64_t)row * ld + col;
-            if (add)
-              atomicAddNoRet(p, acc[mi][ni][r]);
-            else
-              *p = acc[mi][ni][r];
-          }
+          acc[mi][ni][r] =
+              (row < row_lim && col < col_lim) ? in[(int64_t)row * ld + col] : 0.f;
+        }
+  }
+}
+
+// Writes this wave's 128 x 64 accumulators to a row-major fp32 matrix out[rows][ld] at
+// (row0, col0); rows >= row_lim and columns >= col_lim are dropped.  For each register a
+// half-wave writes 32 consecutive columns (128 bytes).
+__device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, int row0,
+                                           int row_lim, int col0, int col_lim, const Acc& acc,
+                                           int lane) {
+  if (row0 + kWaveM <= row_lim && col0 + kWaveN <= col_lim) {
+#pragma unroll
+    for (int mi = 0; mi < kMB; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNB; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          out[(int64_t)(row0 + 32 * mi + acc_row(r, lane)) * ld + col0 + 32 * ni + (lane & 31)] =
+              acc[mi][ni][r];
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < kMB; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNB; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + 32 * mi + acc_row(r, lane), col = col0 + 32 * ni + (lane & 31);
+          if (row < row_lim && col < col_lim) out[(int64_t)row * ld + col] = acc[mi][ni][r];
         }
   }
 }
@@ -696,9 +704,15 @@ __device__ __forceinline__ void tile_bwd_de(const BwdArgs<T>& A, int lin, const 
   build_stage_list<KS, NST>(flags, fstride, n_stages, true, tb * 4, sList, sCnt, seg);
   const int n_act = seg[0] + seg[1] + seg[2];
 
-  Acc acc;
-  zero_acc(acc);
+  // dE of this tile accumulates over the chunks: the running sum is read into the
+  // accumulators up front (its latency overlaps the pipeline's first loads) and written back
+  // with plain stores; one workgroup per tile and launch, launches in stream order
   if (n_act == 0 && accumulate) return;
+  Acc acc;
+  if (accumulate)
+    load_tile(dE, D, tok0 + kWaveM * wm, N, d0 + kWaveN * wn, D, acc, lane);
+  else
+    zero_acc(acc);
   const int ldb = D * (int)sizeof(T);
   uint32_t offA[I], offB[I];
   kmajor_offsets<KB>(offA, (int)ldg * (int)sizeof(T), wave, lane);
@@ -721,7 +735,7 @@ __device__ __forceinline__ void tile_bwd_de(const BwdArgs<T>& A, int lin, const 
         [=, &offB](char* l, int q0, int q1) { mn_issue<T, KB>(rb, offB, 0u, l, wave, lane, q0, q1); });
   };
   run_segments<T, KB, NST, true, false>(seg, issue, B, acc, wm, wn, lane);
-  store_tile(dE, D, tok0 + kWaveM * wm, N, d0 + kWaveN * wn, D, acc, lane, accumulate != 0);
+  store_tile(dE, D, tok0 + kWaveM * wm, N, d0 + kWaveN * wn, D, acc, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -783,8 +797,7 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
     store_tile_bf16((__bf16*)A.dC + dc_off, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc,
                     lane);
   else
-    store_tile((float*)A.dC + dc_off, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc, lane,
-               false);
+    store_tile((float*)A.dC + dc_off, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc, lane);
 }
 
 // Work items of the backward launches: one per tile (grouped_tile).
