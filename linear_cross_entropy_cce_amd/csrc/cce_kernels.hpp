@@ -425,10 +425,34 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
 
   // The wave's 64 token columns are one filter block wide and its 128 vocabulary rows two
   // blocks (a = 0, 1: register blocks mi = 2a, 2a + 1).  Each block is finished in turn --
-  // G, the wave-wide keep decision, its flag, its store -- so the stores of the first block
-  // are in flight while the second is computed.
+  // G, the wave-wide keep decision, its flag -- then its values go out.
+  //
+  // bf16 G goes out through LDS: a lane's registers hold 4 consecutive vocabulary entries of
+  // one token (8 bytes), and the 64 lanes of a store would touch 64 token rows of G.  Each wave
+  // instead writes its 128 x 64 block, token-major, into its own 16 KB of the (now idle) stage
+  // buffers, then stores 16 bytes per lane, 256 contiguous bytes per token.  The 16-byte chunk c
+  // of token row n sits at chunk c ^ (n % 16), which keeps both LDS passes free of bank
+  // conflicts.
+  constexpr bool kStaged = sizeof(T) == 2 && 2 * NST * Geo<KB>::kOpBytes >= kWaves * 16384;
   int n_skipped = 0;
   const int nblk = tok0 + kWaveN * wn;          // token start of the wave's block
+  bool kept[2] = {false, false};
+  lds_char_t* stg = nullptr;                    // this wave's 16 KB of LDS
+  if constexpr (kStaged) {
+    constexpr int kPer = Geo<KB>::kOpBytes / 16384;   // waves per operand buffer
+    const int buf = wave / kPer;
+    // LDS addresses of the operand buffers, chosen as integers (a choice between the generic
+    // pointers would hide from the compiler that the pipeline's reads are LDS reads)
+    uint32_t base = 0;
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      const uint32_t la = (uint32_t)(uintptr_t)(lds_char_t*)B.a[i];
+      const uint32_t lb = (uint32_t)(uintptr_t)(lds_char_t*)B.b[i];
+      base = buf == 2 * i ? la : buf == 2 * i + 1 ? lb : base;
+    }
+    stg = (lds_char_t*)(uintptr_t)(base + (wave % kPer) * 16384);
+    stage_barrier();   // every wave has read its last stage (each waited for its own loads)
+  }
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     float pmax[kNB];
@@ -472,7 +496,27 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
     const bool keep = in_range && (!filter || __ballot(sig) != 0ull);
     if (in_range && !keep) ++n_skipped;
     if (lane == 0) flags[(int64_t)(nblk >> 6) * fstride + (vblk >> 6)] = keep ? 0 : 1;
+    kept[a] = keep;
     if (!keep) continue;
+    if constexpr (kStaged) {
+      typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+#pragma unroll
+      for (int mi = 2 * a; mi < 2 * a + 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < kNB; ++ni) {
+          const int nl = 32 * ni + (lane & 31);
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int c = 4 * mi + rq;   // vocabulary entries 8c .. 8c + 7 of the wave's rows
+            bf16x4_t v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (__bf16)acc[mi][ni][4 * rq + i];
+            *(__attribute__((address_space(3))) bf16x4_t*)(stg + nl * 256 + ((c ^ (nl & 15)) << 4) +
+                                                           8 * (lane >> 5)) = v;
+          }
+        }
+      continue;
+    }
     // store: 4 consecutive vocab rows of one token per lane and register group
 #pragma unroll
     for (int mi = 2 * a; mi < 2 * a + 2; ++mi)
@@ -497,6 +541,21 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
           }
         }
       }
+  }
+  if constexpr (kStaged) {
+    // 4 tokens per store, 16 lanes per token row (256 bytes); chunks 0..7 belong to block 0
+    const int c = lane & 15;
+    const bool mine = c < 8 ? kept[0] : kept[1];
+    if (kept[0] || kept[1]) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int nl = 4 * i + (lane >> 4);
+        const bf16x8_t v =
+            *(const __attribute__((address_space(3))) bf16x8_t*)(stg + nl * 256 + ((c ^ (nl & 15)) << 4));
+        if (mine)
+          *(bf16x8_t*)(G + (int64_t)(nblk + nl) * ldg + vl0 + kWaveM * wm + 8 * c) = v;
+      }
+    }
   }
   if (skip_count && lane == 0 && n_skipped) atomicAdd(skip_count, (unsigned long long)n_skipped);
 }
