@@ -778,9 +778,15 @@ __device__ __forceinline__ void tile_bwd_de(const BwdArgs<T>& A, int lin, const 
   mn_offsets<T, KB>(offB, ldb, d0, D, wave, lane);
   const T* gt = G + (int64_t)tok0 * ldg;
   const int g_rec = kTile * (int)ldg * (int)sizeof(T);
+  // issue(i) is called once per i, in order: each call reads the list entry of the next one,
+  // so no call waits for an LDS read (the empty asm keeps the compiler from working on the
+  // next entry as soon as it arrives, which would wait for the LDS reads issued since)
+  int next_e = sList[0];
   auto issue = [&](int i) {
     const bool live = i < n_act;   // past the end of the list: zeros
-    const int e = __builtin_amdgcn_readfirstlane(sList[live ? i : 0]);
+    asm volatile("" : "+v"(next_e));
+    const int e = __builtin_amdgcn_readfirstlane(next_e);
+    next_e = sList[i + 1 < n_act ? i + 1 : 0];
     const int k0 = (e >> 4) * KS;
     const bool zero = (e >> (wave >> 1)) & 1;  // wave w loads token rows 32 w .. 32 w + 31
     const Rsrc ra = make_rsrc(gt, (zero || !live) ? 0 : g_rec);
@@ -836,9 +842,12 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
     build_stage_list<KS, NST>(flags + (int64_t)((sbase * KS) >> 6) * fstride, fstride, cnt,
                               false, vt * 4, sList, sCnt, seg);
     const int n_act = seg[0] + seg[1] + seg[2];
+    int next_e = sList[0];   // list entry of the next issue() call (calls come in order)
     auto issue = [&](int i) {
       const bool live = i < n_act;   // past the end of the list: zeros
-      const int e = __builtin_amdgcn_readfirstlane(sList[live ? i : 0]);
+      asm volatile("" : "+v"(next_e));
+      const int e = __builtin_amdgcn_readfirstlane(next_e);
+      next_e = sList[i + 1 < n_act ? i + 1 : 0];
       const int k0 = (sbase + (e >> 4)) * KS;
       const uint32_t zc = (uint32_t)(e & 15);
       const Rsrc ra = mn_rsrc<T, KB>(

@@ -153,8 +153,9 @@ __device__ __forceinline__ void kmajor_offsets(uint32_t (&off)[Geo<KB>::kIssue],
 // leaves the row test unchanged (a chunk never reaches past its own row).
 __device__ __forceinline__ Rsrc kmajor_rsrc(const void* origin, int rows_left,
                                                               int ld_bytes) {
-  const int rows = rows_left < 0 ? 0 : (rows_left > kTile ? kTile : rows_left);
-  return make_rsrc(origin, rows * ld_bytes);
+  const int rows = rows_left < kTile ? rows_left : kTile;   // min, multiply, max (no med3)
+  const int rec = rows * ld_bytes;
+  return make_rsrc(origin, rec > 0 ? rec : 0);
 }
 
 // Instructions [q0, q1) of this wave's share of a stage at byte offset soff along K.
@@ -208,9 +209,12 @@ template <typename T, int KB>
 __device__ __forceinline__ Rsrc mn_rsrc(const void* origin, int rows_left,
                                                           int ld_bytes, int col0_bytes) {
   constexpr int R = KB / (int)sizeof(T);
-  const int rows = rows_left < 0 ? 0 : (rows_left > R ? R : rows_left);
+  // min, multiply, then max (a clamp of the row count would become a vector med3 and pull the
+  // rest of the arithmetic onto the VALU); a negative row count gives a negative, then empty,
+  // range
+  const int rows = rows_left < R ? rows_left : R;
   const int rec = rows * ld_bytes - col0_bytes;
-  return make_rsrc(origin, rec < 0 ? 0 : rec);
+  return make_rsrc(origin, rec > 0 ? rec : 0);
 }
 
 // Instructions [q0, q1).  zero_cols bit b = load zeros for columns 64 b .. 64 b + 63.
@@ -315,7 +319,9 @@ __device__ __forceinline__ void mma(f32x16_t& acc, const f32x4_t& a, const f32x4
 }
 
 struct NoIssue {
-  __device__ __forceinline__ void one(int) const {}
+  __device__ __forceinline__ NoIssue make() const { return *this; }
+  template <typename St>
+  __device__ __forceinline__ void one(const St&, int) const {}
 };
 
 // Pins an accumulator in the instruction order.  MFMA builtins have no side effects, so the
@@ -325,10 +331,11 @@ struct NoIssue {
 __device__ __forceinline__ void pin(f32x16_t& acc) { asm volatile("" : "+v"(acc)); }
 
 // One stage of MFMAs for this wave: KB / 32 k-groups x 4 x 2 blocks.  While the 8 MFMAs of the
-// first k-group run, part.one(j) issues the j-th load of a later stage, one after each MFMA,
-// so the address units never stall the MFMA issue and the loads get the rest of the stage to
-// land.  The fragments of group g + 1 are read while group g runs.  Scheduling barriers and
-// the accumulator pins keep this order.
+// first k-group run, the loads of a later stage go out, one after each MFMA, so the address
+// units never stall the MFMA issue and the loads get the rest of the stage to land.  The
+// later stage's addresses (part.make(): descriptors, list lookups) are worked out after the
+// first MFMA has issued, off the path to it.  The fragments of group g + 1 are read while group
+// g runs.  Scheduling barriers and the accumulator pins keep this order.
 template <typename T, int KB, bool AK, bool BK, typename Part = NoIssue>
 __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Acc& acc, int wm,
                                               int wn, int lane, const Part& part = Part()) {
@@ -346,8 +353,29 @@ __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Ac
   read_a(0, 0);
   read_b(0, 0);
   __builtin_amdgcn_sched_barrier(0);
+  // k-group 0: MFMA j, then load j; the pins keep MFMA j after load j - 1 and before load j
+  if (G > 1) {
+    read_a(1, 1);
+    read_b(1, 1);
+  }
+  pin(acc[0][0]);
+  mma(acc[0][0], a[0][0], b[0][0]);
+  pin(acc[0][0]);
+  __builtin_amdgcn_sched_barrier(0);
+  const auto st = part.make();
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int j = 0; j < kMB * kNB; ++j) {
+    const int mi = j / kNB, ni = j % kNB;
+    if (j > 0) {
+      pin(acc[mi][ni]);
+      mma(acc[mi][ni], a[0][mi], b[0][ni]);
+      pin(acc[mi][ni]);
+    }
+    part.one(st, j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int g = 1; g < G; ++g) {
     const int ca = g & 1, cb = g & 1;
     if (g + 1 < G) {
       read_a((g + 1) & 1, g + 1);
@@ -356,18 +384,7 @@ __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Ac
 #pragma unroll
     for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < kNB; ++ni) {
-        if (g == 0) {
-          // MFMA j, then load j: the pins keep MFMA j after load j - 1 and before load j
-          pin(acc[mi][ni]);
-          mma(acc[mi][ni], a[ca][mi], b[cb][ni]);
-          pin(acc[mi][ni]);
-          part.one(kNB * mi + ni);
-          __builtin_amdgcn_sched_barrier(0);
-        } else {
-          mma(acc[mi][ni], a[ca][mi], b[cb][ni]);
-        }
-      }
+      for (int ni = 0; ni < kNB; ++ni) mma(acc[mi][ni], a[ca][mi], b[cb][ni]);
     __builtin_amdgcn_sched_barrier(0);
   }
   // every MFMA of the stage before whatever follows (the next stage's wait and barrier)
@@ -409,13 +426,17 @@ __device__ __forceinline__ void wait_stages(int keep) {
   }
 }
 
-// Loads of one later stage, spread over the MFMAs of the current one (compute_stage).
-template <int KB, typename St>
+// Loads of one later stage, spread over the MFMAs of the current one (compute_stage):
+// make() prepares the stage (issue(i)), one(st, j) issues its j-th load.
+template <int KB, typename Issue>
 struct StagePart {
-  const St& st;
+  Issue& issue;
+  int i;
   char* na;
   char* nb;
-  __device__ __forceinline__ void one(int j) const {
+  __device__ __forceinline__ auto make() const { return issue(i); }
+  template <typename St>
+  __device__ __forceinline__ void one(const St& st, int j) const {
     if (j < 2 * Geo<KB>::kIssue) st.one(na, nb, j);
   }
 };
@@ -434,8 +455,7 @@ __device__ __forceinline__ void run_round(int g0, Issue& issue, const Bufs<NST>&
     // stage g0 + u has landed once at most P - 1 later stages are still in flight
     wait_stages<KB, NST>(P - 1);
     stage_barrier();
-    const auto st = issue(g0 + u + P);   // per-stage address setup, once
-    const StagePart<KB, decltype(st)> part{st, B.a[(u + P) % NST], B.b[(u + P) % NST]};
+    const StagePart<KB, Issue> part{issue, g0 + u + P, B.a[(u + P) % NST], B.b[(u + P) % NST]};
     compute_stage<T, KB, AK, BK>(B.a[u], B.b[u], acc, wm, wn, lane, part);
   }
 }
