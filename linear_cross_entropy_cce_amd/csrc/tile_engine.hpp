@@ -78,7 +78,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 // chunk lands in its fixed LDS slot.
 // ---------------------------------------------------------------------------------------
 constexpr uint32_t kOob = 0x80000000u;         // offset answered with zeros
-constexpr int kRecords = 0x7FFFFFF0;           // descriptor range
 
 // Buffer descriptor (V#) of a raw buffer: base address (48 bits, stride 0), byte range, and the
 // same format word as the compiler's buffer-resource builtin.  Base and range are
@@ -136,7 +135,7 @@ __device__ __forceinline__ int kmajor_chunk(int r, int lane) {
 }
 
 // Offsets of this lane's chunks relative to the tile origin (row0, k0).  Rows past the
-// operand's end are cut off by the descriptor range (tile_records), not here.
+// operand's end are cut off by the descriptor range (kmajor_rsrc), not here.
 template <int KB>
 __device__ __forceinline__ void kmajor_offsets(uint32_t (&off)[Geo<KB>::kIssue], int64_t ld_bytes,
                                                int wave, int lane) {
@@ -318,12 +317,6 @@ __device__ __forceinline__ void mma(f32x16_t& acc, const f32x4_t& a, const f32x4
   for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], acc, 0, 0, 0);
 }
 
-struct NoIssue {
-  __device__ __forceinline__ NoIssue make() const { return *this; }
-  template <typename St>
-  __device__ __forceinline__ void one(const St&, int) const {}
-};
-
 // Pins an accumulator in the instruction order.  MFMA builtins have no side effects, so the
 // code generator may move them across loads and barriers; an (empty) volatile asm statement
 // that reads and writes the accumulator cannot move relative to other side effects, and the
@@ -336,9 +329,9 @@ __device__ __forceinline__ void pin(f32x16_t& acc) { asm volatile("" : "+v"(acc)
 // later stage's addresses (part.make(): descriptors, list lookups) are worked out after the
 // first MFMA has issued, off the path to it.  The fragments of group g + 1 are read while group
 // g runs.  Scheduling barriers and the accumulator pins keep this order.
-template <typename T, int KB, bool AK, bool BK, typename Part = NoIssue>
+template <typename T, int KB, bool AK, bool BK, typename Part>
 __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Acc& acc, int wm,
-                                              int wn, int lane, const Part& part = Part()) {
+                                              int wn, int lane, const Part& part) {
   typedef typename Traits<T>::frag_t F;
   constexpr int G = Geo<KB>::kGroups;
   F a[2][kMB], b[2][kNB];
