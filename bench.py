@@ -258,6 +258,72 @@ def shards_compare(workload: str, n_shards: int, steps: int, warmup: int) -> int
     return 0
 
 
+def vocab_order_compare(workload: str, steps: int, warmup: int) -> int:
+    """A fwd+bwd step on the workload as given and on the same problem with the vocabulary
+    relabelled (one JSON line): the classifier rows sorted by decreasing L2 norm and the targets
+    mapped accordingly, which gathers the rows that carry most of the softmax into few
+    vocabulary tiles, so whole K stages of the gradient products are skipped.  The relabelling
+    is the caller's (done here with torch, outside the timed region; a training loop would keep
+    its classifier in that order); the loss and dE are unchanged and dC comes back in the new
+    row order.  The results of the two runs are compared, untimed."""
+    import torch
+
+    import cce_synth as S
+    import linear_cross_entropy_cce_amd as cce
+    w = S.WORKLOADS[workload]
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = S.make_inputs(w)
+    E = torch.from_numpy(d["E"]).to(dev, tdt)
+    C = torch.from_numpy(d["C"]).to(dev, tdt)
+    t = torch.from_numpy(d["targets"]).to(dev)
+    dl = torch.full((w.N,), 1.0 / w.N, dtype=torch.float32, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    perm = torch.argsort(torch.linalg.vector_norm(C.float(), dim=1), descending=True)
+    rank = torch.empty_like(perm)
+    rank[perm] = torch.arange(w.V, device=dev)
+    Cp = C[perm].contiguous()
+    tp = torch.where(t == S.IGNORE_INDEX, t, rank[t.clamp(min=0)])
+    b.record()
+    torch.cuda.synchronize()
+    out = {"workload": f"{w.name}: N={w.N} D={w.D} V={w.V} {w.dtype}, filter_eps={w.filter_eps:g}",
+           "order": "classifier rows by decreasing L2 norm",
+           "relabel_ms_untimed": a.elapsed_time(b)}
+    res = {}
+    for name, CC, tt in (("as_given", C, t), ("relabelled", Cp, tp)):
+        stats = torch.zeros(2, dtype=torch.int64, device=dev)
+
+        def step():
+            loss, lse = cce.cce_forward(E, CC, tt, S.IGNORE_INDEX)
+            dE, dC = cce.cce_backward(dl, E, CC, tt, lse, S.IGNORE_INDEX, w.filter_eps,
+                                      skip_stats=stats)
+            return loss, dE, dC
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        cce.timing_begin(max_launches=steps * 200)
+        a.record()
+        for _ in range(steps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        k = cce.timing_end()
+        skipped, total = (int(x) for x in stats.tolist())
+        out[name] = {"ms_per_step": a.elapsed_time(b) / steps,
+                     "kernel_ms_per_step": {kk: v[0] / steps for kk, v in k.items()},
+                     "skip_fraction_64x64_blocks": skipped / total if total else 0.0}
+        res[name] = step()
+    (l0, e0, c0), (l1, e1, c1) = res["as_given"], res["relabelled"]
+    torch.cuda.synchronize()
+    rel = lambda x, y: float((x - y).norm() / y.norm().clamp(min=1e-30))
+    out["relabelled_vs_as_given"] = {"loss_max_abs": float((l1 - l0).abs().max()),
+                                     "dE_rel": rel(e1, e0), "dC_rel": rel(c1, c0[perm])}
+    out["speedup"] = out["as_given"]["ms_per_step"] / out["relabelled"]["ms_per_step"]
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +340,9 @@ def main() -> int:
     ap.add_argument("--memory-compare", action="store_true",
                     help="only compare peak device memory of a materialising PyTorch head with "
                          "libcce at the workload's shape (one JSON line)")
+    ap.add_argument("--vocab-order", action="store_true",
+                    help="only time the workload with its vocabulary relabelled by classifier "
+                         "row norm against the workload as given (one JSON line)")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the GPU clock / power sampling after the timed region")
     ap.add_argument("--no-gemm-ref", action="store_true",
@@ -288,6 +357,8 @@ def main() -> int:
         return memory_compare(args.workload)
     if args.shards:
         return shards_compare(args.workload, args.shards, args.steps, args.warmup)
+    if args.vocab_order:
+        return vocab_order_compare(args.workload, args.steps, args.warmup)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

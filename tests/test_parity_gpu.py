@@ -274,3 +274,28 @@ def test_stages_with_one_live_half(dtype, N):
     _, _, (sk, tot) = oracle.backward(d["E"], d["C"], d["targets"],
                                       S.dloss_weights(71, N), II, filter_eps=EPS)
     assert g["skipped"] == sk and 0.3 * tot < sk < 0.6 * tot, (g["skipped"], sk, tot)
+
+
+def test_vocabulary_relabelled_by_row_norm():
+    """The caller-side relabelling that bench.py --vocab-order times: classifier rows sorted by
+    decreasing norm and the targets mapped, which gathers the rows carrying the softmax into few
+    blocks.  Loss, LSE and dE are those of the problem as given (oracle), dC is its rows in the
+    new order, and more blocks are skipped than for the problem as given."""
+    w = S.Workload("sparse_small", 320, 128, 3000, "bf16", 12.0, 1.2, boost_frac=0.05, seed=3)
+    d = S.make_inputs(w)
+    C, t = d["C"], d["targets"]
+    perm = np.argsort(-np.linalg.norm(C.astype(np.float64), axis=1), kind="stable")
+    rank = np.empty_like(perm)
+    rank[perm] = np.arange(len(perm))
+    relabelled = {"E": d["E"], "C": C[perm], "targets": np.where(t == II, t, rank[np.maximum(t, 0)])}
+    wts = S.dloss_weights(3, 320)
+    g0 = gpu_run(d, "bf16", wts, EPS)
+    g1 = gpu_run(relabelled, "bf16", wts, EPS)
+    loss, lse = oracle.forward(d["E"], C, t, II)
+    dE, dC, _ = oracle.backward(d["E"], C, t, wts, II)          # unfiltered
+    assert np.abs(g1["loss"] - loss).max() <= LOSS_TOL
+    assert np.abs(g1["lse"] - lse).max() <= LOSS_TOL
+    assert rel(g1["dE"], dE) <= GRAD_TOL, rel(g1["dE"], dE)
+    assert rel(g1["dC"], dC[perm]) <= GRAD_TOL, rel(g1["dC"], dC[perm])
+    log(f"[relabelled] skipped {g1['skipped']}/{g1['total']} (as given {g0['skipped']})")
+    assert g1["skipped"] > g0["skipped"]
