@@ -17,8 +17,10 @@
  *   - targets is int64 [N]; a row whose target equals ignore_index is "ignored": its loss is 0,
  *     its gradient rows are 0, and it never makes a filter block significant.
  *   - All array arguments are device pointers into memory the caller owns (hipMalloc or a
- *     framework allocator), 16-byte aligned.  The library never allocates or frees device memory and keeps no
- *     per-call state; scratch memory is the caller's workspace (query its size first).
+ *     framework allocator).  E, C, dE, dC and the workspace must be 16-byte aligned (the
+ *     kernels move them in 16-byte vectors); a misaligned one is rejected with
+ *     CCE_ERR_INVALID_ARGUMENT.  The library never allocates or frees device memory and keeps
+ *     no per-call state; scratch memory is the caller's workspace (query its size first).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work on
  *     that stream and returns; no host synchronisation happens inside.  Calls that share a
  *     workspace must not run concurrently on different streams.

@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <vector>
 
 #include "cce.h"
@@ -48,6 +49,14 @@ bool sizes_ok(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
   if (D % (dt == CCE_BF16 ? 8 : 4) != 0) return false;
   return true;
 }
+// The kernels move E, C, the gradients and the workspace in 16-byte vectors.
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+bool all_aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned16(p)) return false;
+  return true;
+}
+
 bool sizes_supported(int64_t N, int64_t V, int64_t D) {
   return N <= kMaxRows && V <= kMaxRows && D <= kMaxD;
 }
@@ -298,6 +307,7 @@ cce_status cce_forward(const void* E, const void* C, const int64_t* targets, int
   if (!sizes_supported(N, V, D)) return CCE_ERR_UNSUPPORTED;
   if (N == 0) return CCE_OK;
   if (!E || !C || !targets || !loss || !lse || !ws) return CCE_ERR_INVALID_ARGUMENT;
+  if (!all_aligned16({E, C, ws})) return CCE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < fwd_bytes(N, V)) return CCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   if (dt == CCE_BF16)
@@ -326,7 +336,7 @@ cce_status backward_entry(const float* dloss, int64_t dloss_stride, const void* 
   if (voff < 0) return CCE_ERR_INVALID_ARGUMENT;
   if (N == 0) {
     // nothing to reduce: dC is still defined (all zero) and so are the statistics
-    if (!dC) return CCE_ERR_INVALID_ARGUMENT;
+    if (!dC || !aligned16(dC)) return CCE_ERR_INVALID_ARGUMENT;
     hipStream_t st = (hipStream_t)stream;
     const int64_t n = V * D * (int64_t)dtype_size(grad_dtype) / 4;   // 4-byte words
     hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)std::min<int64_t>(ceil_div(n, 1024), 4096)),
@@ -340,6 +350,7 @@ cce_status backward_entry(const float* dloss, int64_t dloss_stride, const void* 
   }
   if (!dloss || !E || !C || !targets || !lse || !dE || !dC || !ws)
     return CCE_ERR_INVALID_ARGUMENT;
+  if (!all_aligned16({E, C, dE, dC, ws})) return CCE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < bwd_layout(N, V, D, dt).total) return CCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   if (dt == CCE_BF16)
@@ -385,6 +396,7 @@ cce_status cce_forward_shard(const void* E, const void* C, const int64_t* target
   if (N == 0) return CCE_OK;
   if (!E || !C || !targets || !lse_shard || !target_logit || !ws)
     return CCE_ERR_INVALID_ARGUMENT;
+  if (!all_aligned16({E, C, ws})) return CCE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < fwd_bytes(N, V)) return CCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   if (dt == CCE_BF16)
@@ -421,6 +433,8 @@ cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, i
   if (!std::isfinite(filter_eps) || filter_eps < 0.f) return CCE_ERR_INVALID_ARGUMENT;
   if (!loss_mean || !dC || !ws) return CCE_ERR_INVALID_ARGUMENT;
   if (N > 0 && (!E || !C || !targets || !dE)) return CCE_ERR_INVALID_ARGUMENT;
+  if (!all_aligned16({dC, ws}) || (N > 0 && !all_aligned16({E, C, dE})))
+    return CCE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < cce_loss_mean_workspace_bytes(N, V, D, dt)) return CCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   if (grad_dtype != CCE_F32 && grad_dtype != CCE_BF16) return CCE_ERR_INVALID_ARGUMENT;

@@ -113,6 +113,8 @@ def test_forward_validation(lib):
     assert call(args(wsb=ok_ws - 1)) == 3
     assert call(args(N=1 << 25)) == 2
     assert call(args(N=0, E=None, C=None, t=None, loss=None, lse=None, ws=None)) == 0
+    for name in ("E", "C", "ws"):                      # 16-byte vectors: misaligned -> rejected
+        assert call(args(**{name: ctypes.c_void_p(0x1008)})) == 1
 
 
 def test_backward_validation(lib):
@@ -130,6 +132,9 @@ def test_backward_validation(lib):
     assert call(lse=None) == 1
     assert call(wsb=ok_ws - 1) == 3
     assert call(D=4) == 1
+    for name in ("E", "C", "dE", "dC", "ws"):
+        assert call(**{name: ctypes.c_void_p(0x2004)}) == 1
+    assert call(N=0, dC=ctypes.c_void_p(0x2004)) == 1
 
 
 def test_loss_mean_validation(lib):
@@ -142,6 +147,8 @@ def test_loss_mean_validation(lib):
     assert call(mean=None) == 1
     assert call(wsb=ok_ws - 1) == 3
     assert call(eps=-0.5) == 1
+    for name in ("E", "C", "dE", "dC", "ws"):
+        assert call(**{name: ctypes.c_void_p(0x3002)}) == 1
     assert ok_ws >= (lib.cce_forward_workspace_bytes(16, 100, 64, 1)
                      + lib.cce_backward_workspace_bytes(16, 100, 64, 1))
 
