@@ -299,3 +299,16 @@ def test_vocabulary_relabelled_by_row_norm():
     assert rel(g1["dC"], dC[perm]) <= GRAD_TOL, rel(g1["dC"], dC[perm])
     log(f"[relabelled] skipped {g1['skipped']}/{g1['total']} (as given {g0['skipped']})")
     assert g1["skipped"] > g0["skipped"]
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 270000), ("f32", 140000)])
+def test_dc_stage_lists_in_several_pieces(dtype, N):
+    """Token counts past one dC stage list (4096 stages of 64 bf16 or 32 fp32 tokens): the dC
+    product builds and runs its list piece by piece, here with stages live in one half, both or
+    neither, against the oracle with exactly its skipped blocks."""
+    V, D = 1000, 64
+    d = _half_live_case(N, V, D, dtype, 73)
+    w = S.dloss_weights(73, N)
+    g = check_against_oracle(d, dtype, w, EPS, f"pieces_{dtype}")
+    _, _, (sk, tot) = oracle.backward(d["E"], d["C"], d["targets"], w, II, filter_eps=EPS)
+    assert g["skipped"] == sk, (g["skipped"], sk, tot)
