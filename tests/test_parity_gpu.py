@@ -312,3 +312,15 @@ def test_dc_stage_lists_in_several_pieces(dtype, N):
     g = check_against_oracle(d, dtype, w, EPS, f"pieces_{dtype}")
     _, _, (sk, tot) = oracle.backward(d["E"], d["C"], d["targets"], w, II, filter_eps=EPS)
     assert g["skipped"] == sk, (g["skipped"], sk, tot)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_last_vocabulary_chunk_narrower_than_a_block(dtype):
+    """V = 8192 + 40: the second backward chunk is 40 rows, less than one 64-row filter block
+    and one 256-row tile (its G tile, flags, dE stages and dC tile are all ragged)."""
+    D = 72 if dtype == "bf16" else 68
+    d = S.small_case(300, D, 8192 + 40, dtype, 29, 3.0, 1.1, 0.05)
+    t = d["targets"].copy()
+    t[::7] = 8192 + np.arange(len(t[::7])) % 40          # targets inside the narrow chunk
+    d["targets"] = t
+    check_against_oracle(d, dtype, S.dloss_weights(29, 300), EPS, f"narrow_chunk_{dtype}")
