@@ -324,3 +324,26 @@ def test_last_vocabulary_chunk_narrower_than_a_block(dtype):
     t[::7] = 8192 + np.arange(len(t[::7])) % 40          # targets inside the narrow chunk
     d["targets"] = t
     check_against_oracle(d, dtype, S.dloss_weights(29, 300), EPS, f"narrow_chunk_{dtype}")
+
+
+def test_ignore_index_inside_the_vocabulary():
+    """ignore_index may be a real token id (here 3, frequent under Zipf targets): every row
+    whose target equals it is ignored (loss 0, zero dE row, no part in dC or the filter), and
+    the other rows are scored as usual (the inputs hold no -100 targets)."""
+    ii = 3
+    d = S.small_case(400, 64, 1500, "bf16", 41, 3.0, 1.1, 0.0)
+    t = d["targets"]
+    assert (t == ii).sum() > 10
+    w = S.dloss_weights(41, 400)
+    E, C, tt = upload(d, "bf16")
+    loss, lse = cce.cce_forward(E, C, tt, ii)
+    dl = torch.from_numpy(w).to(DEV)
+    dE, dC = cce.cce_backward(dl, E, C, tt, lse, ii, EPS)
+    torch.cuda.synchronize()
+    rl, rlse = oracle.forward(d["E"], d["C"], t, ii)
+    rE, rC, _ = oracle.backward(d["E"], d["C"], t, w, ii)
+    g_loss, g_dE = loss.cpu().numpy(), dE.cpu().numpy()
+    assert np.abs(g_loss - rl).max() <= LOSS_TOL
+    assert np.abs(lse.cpu().numpy() - rlse).max() <= LOSS_TOL
+    assert np.all(g_loss[t == ii] == 0.0) and np.all(g_dE[t == ii] == 0.0)
+    assert rel(g_dE, rE) <= GRAD_TOL and rel(dC.cpu().numpy(), rC) <= GRAD_TOL
