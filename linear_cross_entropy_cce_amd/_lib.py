@@ -101,6 +101,8 @@ def _check_inputs(E, C, targets):
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+        if t.device != E.device:
+            raise ValueError(f"{name} is on {t.device}, E on {E.device}")
     if E.dim() != 2 or C.dim() != 2 or E.shape[1] != C.shape[1]:
         raise ValueError(f"E [N,D] and C [V,D] expected, got {tuple(E.shape)}, {tuple(C.shape)}")
     if E.dtype != C.dtype:
@@ -108,6 +110,13 @@ def _check_inputs(E, C, targets):
     if targets.dtype != torch.int64 or targets.shape != (E.shape[0],):
         raise ValueError("targets must be int64 [N]")
     return E.shape[0], C.shape[0], E.shape[1], dtype_code(E.dtype)
+
+
+def _check_vec(name, t, n, dtype, dev):
+    """A caller-supplied per-token array: contiguous, dtype, [n], on the inputs' device."""
+    if (t.dtype != dtype or tuple(t.shape) != (n,) or not t.is_contiguous() or not t.is_cuda
+            or t.device != dev):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor [{n}] on {dev}")
 
 
 def forward_workspace_bytes(N: int, V: int, D: int, dtype: torch.dtype) -> int:
@@ -141,11 +150,14 @@ def cce_forward(E, C, targets, ignore_index: int = -100, *, loss=None, lse=None,
     dev = E.device
     loss = torch.empty(N, dtype=torch.float32, device=dev) if loss is None else loss
     lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else lse
+    _check_vec("loss", loss, N, torch.float32, dev)
+    _check_vec("lse", lse, N, torch.float32, dev)
     need = lib().cce_forward_workspace_bytes(N, V, D, dt)
     ws = workspace(need, dev) if ws is None else ws
-    _check("cce_forward", lib().cce_forward(
-        _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, _ptr(loss), _ptr(lse),
-        _ptr(ws), ws.numel() * ws.element_size(), _ptr(err_flag), _stream(stream)))
+    with torch.cuda.device(dev):
+        _check("cce_forward", lib().cce_forward(
+            _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, _ptr(loss), _ptr(lse),
+            _ptr(ws), ws.numel() * ws.element_size(), _ptr(err_flag), _stream(stream)))
     return loss, lse
 
 
@@ -170,13 +182,15 @@ def cce_backward(dloss, E, C, targets, lse, ignore_index: int = -100, filter_eps
     stride = 0 if dloss.numel() == 1 and N != 1 else 1
     if stride == 1 and dloss.shape != (N,):
         raise ValueError("dloss must have N elements or one")
+    _check_vec("lse", lse, N, torch.float32, dev)
     dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
     need = lib().cce_backward_workspace_bytes(N, V, D, dt)
     ws = workspace(need, dev) if ws is None else ws
-    _check("cce_backward", lib().cce_backward(
-        _ptr(dloss), stride, _ptr(E), _ptr(C), _ptr(targets), _ptr(lse), N, V, D, dt,
-        ignore_index, float(filter_eps), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
-        ws.numel() * ws.element_size(), _ptr(skip_stats), _stream(stream)))
+    with torch.cuda.device(dev):
+        _check("cce_backward", lib().cce_backward(
+            _ptr(dloss), stride, _ptr(E), _ptr(C), _ptr(targets), _ptr(lse), N, V, D, dt,
+            ignore_index, float(filter_eps), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
+            ws.numel() * ws.element_size(), _ptr(skip_stats), _stream(stream)))
     return dE, dC
 
 
@@ -192,10 +206,11 @@ def cce_loss_mean(E, C, targets, ignore_index: int = -100, filter_eps: float = 0
     dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
     need = lib().cce_loss_mean_workspace_bytes(N, V, D, dt)
     ws = workspace(need, dev) if ws is None else ws
-    _check("cce_loss_mean", lib().cce_loss_mean(
-        _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, float(filter_eps),
-        _ptr(mean), _ptr(n_valid), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
-        ws.numel() * ws.element_size(), _ptr(err_flag), _ptr(skip_stats), _stream(stream)))
+    with torch.cuda.device(dev):
+        _check("cce_loss_mean", lib().cce_loss_mean(
+            _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, float(filter_eps),
+            _ptr(mean), _ptr(n_valid), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
+            ws.numel() * ws.element_size(), _ptr(err_flag), _ptr(skip_stats), _stream(stream)))
     return mean, n_valid, dE, dC
 
 
@@ -207,11 +222,14 @@ def cce_forward_shard(E, C_shard, targets, vocab_offset: int, ignore_index: int 
     dev = E.device
     lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else lse
     zt = torch.empty(N, dtype=torch.float32, device=dev) if target_logit is None else target_logit
+    _check_vec("lse", lse, N, torch.float32, dev)
+    _check_vec("target_logit", zt, N, torch.float32, dev)
     need = lib().cce_forward_workspace_bytes(N, V, D, dt)
     ws = workspace(need, dev) if ws is None else ws
-    _check("cce_forward_shard", lib().cce_forward_shard(
-        _ptr(E), _ptr(C_shard), _ptr(targets), N, V, D, dt, ignore_index, int(vocab_offset),
-        _ptr(lse), _ptr(zt), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    with torch.cuda.device(dev):
+        _check("cce_forward_shard", lib().cce_forward_shard(
+            _ptr(E), _ptr(C_shard), _ptr(targets), N, V, D, dt, ignore_index, int(vocab_offset),
+            _ptr(lse), _ptr(zt), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return lse, zt
 
 
@@ -227,9 +245,12 @@ def cce_merge_shards(lse_shards, target_logits, targets, V_total: int, ignore_in
     dev = lse_shards.device
     loss = torch.empty(N, dtype=torch.float32, device=dev) if loss is None else loss
     lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else lse
-    _check("cce_merge_shards", lib().cce_merge_shards(
-        _ptr(lse_shards), _ptr(target_logits), S, N, _ptr(targets), ignore_index, int(V_total),
-        _ptr(loss), _ptr(lse), _ptr(err_flag), _stream(stream)))
+    _check_vec("loss", loss, N, torch.float32, dev)
+    _check_vec("lse", lse, N, torch.float32, dev)
+    with torch.cuda.device(dev):
+        _check("cce_merge_shards", lib().cce_merge_shards(
+            _ptr(lse_shards), _ptr(target_logits), S, N, _ptr(targets), ignore_index, int(V_total),
+            _ptr(loss), _ptr(lse), _ptr(err_flag), _stream(stream)))
     return loss, lse
 
 
@@ -245,13 +266,15 @@ def cce_backward_shard(dloss, E, C_shard, targets, lse, vocab_offset: int,
     stride = 0 if dloss.numel() == 1 and N != 1 else 1
     if stride == 1 and dloss.shape != (N,):
         raise ValueError("dloss must have N elements or one")
+    _check_vec("lse", lse, N, torch.float32, dev)
     dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
     need = lib().cce_backward_workspace_bytes(N, V, D, dt)
     ws = workspace(need, dev) if ws is None else ws
-    _check("cce_backward_shard", lib().cce_backward_shard(
-        _ptr(dloss), stride, _ptr(E), _ptr(C_shard), _ptr(targets), _ptr(lse), N, V, D, dt,
-        ignore_index, int(vocab_offset), float(filter_eps), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
-        ws.numel() * ws.element_size(), _ptr(skip_stats), _stream(stream)))
+    with torch.cuda.device(dev):
+        _check("cce_backward_shard", lib().cce_backward_shard(
+            _ptr(dloss), stride, _ptr(E), _ptr(C_shard), _ptr(targets), _ptr(lse), N, V, D, dt,
+            ignore_index, int(vocab_offset), float(filter_eps), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
+            ws.numel() * ws.element_size(), _ptr(skip_stats), _stream(stream)))
     return dE, dC
 
 
