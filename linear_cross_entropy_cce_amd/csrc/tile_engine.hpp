@@ -323,36 +323,53 @@ __device__ __forceinline__ void mma(f32x16_t& acc, const f32x4_t& a, const f32x4
 // MFMAs that produce or consume the accumulator stay on their side of it.
 __device__ __forceinline__ void pin(f32x16_t& acc) { asm volatile("" : "+v"(acc)); }
 
-// One stage of MFMAs for this wave: KB / 32 k-groups x 4 x 2 blocks.  While the 8 MFMAs of the
-// first k-group run, the loads of a later stage go out, one after each MFMA, so the address
-// units never stall the MFMA issue and the loads get the rest of the stage to land.  The
-// later stage's addresses (part.make(): descriptors, list lookups) are worked out after the
-// first MFMA has issued, off the path to it.  The fragments of group g + 1 are read while group
-// g runs.  Scheduling barriers and the accumulator pins keep this order.
+// Fragments of two k-groups (slots 0 and 1: group g of a stage lives in slot g % 2).
+template <typename T>
+struct Frags {
+  typename Traits<T>::frag_t a[2][kMB], b[2][kNB];
+};
+
+// The MFMAs of one k-group held in slot `slot`.
+template <typename T>
+__device__ __forceinline__ void mma_group(Acc& acc, const Frags<T>& f, int slot) {
+#pragma unroll
+  for (int mi = 0; mi < kMB; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNB; ++ni) mma(acc[mi][ni], f.a[slot][mi], f.b[slot][ni]);
+}
+
+// One stage of MFMAs for this wave: KB / 32 k-groups x 4 x 2 blocks, with the last k-group
+// carried into the next stage.  Right after the stage's barrier nothing in LDS has been read
+// yet, so the wave starts with the previous stage's last k-group, whose fragments are already
+// in registers (slot 1), while the first fragments of this stage arrive.  Those 8 MFMAs also
+// carry the loads of a later stage, one after each, so the address units never stall the MFMA
+// issue and the loads get the rest of the stage to land; the later stage's addresses
+// (part.make(): descriptors, list lookups) are worked out after the first of them has issued.
+// Then groups 0 .. G - 2 of this stage run, each while the next group's fragments are read;
+// the last group's fragments are read during group G - 2 and waited for before the stage ends,
+// so every read of this stage's LDS buffers is complete at the next barrier (other waves then
+// refill them).  Scheduling barriers and the accumulator pins keep this order.  A stream starts
+// with zero fragments in slot 1 and ends with flush_carried().
 template <typename T, int KB, bool AK, bool BK, typename Part>
-__device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Acc& acc, int wm,
-                                              int wn, int lane, const Part& part) {
-  typedef typename Traits<T>::frag_t F;
+__device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Acc& acc,
+                                              Frags<T>& f, int wm, int wn, int lane,
+                                              const Part& part) {
   constexpr int G = Geo<KB>::kGroups;
-  F a[2][kMB], b[2][kNB];
-  auto read_a = [&](int slot, int g) {
+  static_assert(G % 2 == 0, "the last k-group of a stage lives in slot 1");
+  auto read = [&](int slot, int g) {
 #pragma unroll
-    for (int i = 0; i < kMB; ++i) a[slot][i] = frag<T, KB, AK>(As, kWaveM * wm + 32 * i, g, lane);
-  };
-  auto read_b = [&](int slot, int g) {
+    for (int i = 0; i < kMB; ++i)
+      f.a[slot][i] = frag<T, KB, AK>(As, kWaveM * wm + 32 * i, g, lane);
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) b[slot][i] = frag<T, KB, BK>(Bs, kWaveN * wn + 32 * i, g, lane);
+    for (int i = 0; i < kNB; ++i)
+      f.b[slot][i] = frag<T, KB, BK>(Bs, kWaveN * wn + 32 * i, g, lane);
   };
-  read_a(0, 0);
-  read_b(0, 0);
+  read(0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  // k-group 0: MFMA j, then load j; the pins keep MFMA j after load j - 1 and before load j
-  if (G > 1) {
-    read_a(1, 1);
-    read_b(1, 1);
-  }
+  // the carried k-group: MFMA j, then load j; the pins keep MFMA j after load j - 1 and before
+  // load j
   pin(acc[0][0]);
-  mma(acc[0][0], a[0][0], b[0][0]);
+  mma(acc[0][0], f.a[1][0], f.b[1][0]);
   pin(acc[0][0]);
   __builtin_amdgcn_sched_barrier(0);
   const auto st = part.make();
@@ -361,30 +378,39 @@ __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Ac
     const int mi = j / kNB, ni = j % kNB;
     if (j > 0) {
       pin(acc[mi][ni]);
-      mma(acc[mi][ni], a[0][mi], b[0][ni]);
+      mma(acc[mi][ni], f.a[1][mi], f.b[1][ni]);
       pin(acc[mi][ni]);
     }
     part.one(st, j);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int g = 1; g < G; ++g) {
-    const int ca = g & 1, cb = g & 1;
-    if (g + 1 < G) {
-      read_a((g + 1) & 1, g + 1);
-      read_b((g + 1) & 1, g + 1);
-    }
-#pragma unroll
-    for (int mi = 0; mi < kMB; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < kNB; ++ni) mma(acc[mi][ni], a[ca][mi], b[cb][ni]);
+  for (int g = 0; g + 1 < G; ++g) {
+    read((g + 1) & 1, g + 1);
+    mma_group(acc, f, g & 1);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // every MFMA of the stage before whatever follows (the next stage's wait and barrier)
+  // the last group's fragments are in registers before the stage ends
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  // every MFMA issued so far before whatever follows (the next stage's wait and barrier)
 #pragma unroll
   for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
     for (int ni = 0; ni < kNB; ++ni) pin(acc[mi][ni]);
+}
+
+// Start and end of a stream of compute stages: no carried k-group yet (zero fragments add
+// nothing), and the last stage's carried k-group.
+template <typename T>
+__device__ __forceinline__ void clear_carried(Frags<T>& f) {
+#pragma unroll
+  for (int i = 0; i < kMB; ++i) f.a[1][i] = typename Traits<T>::frag_t{};
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) f.b[1][i] = typename Traits<T>::frag_t{};
+}
+template <typename T>
+__device__ __forceinline__ void flush_carried(Acc& acc, const Frags<T>& f) {
+  mma_group(acc, f, 1);
 }
 
 // Workgroup barrier between pipeline stages.  Each wave has already waited (vmcnt) for its
@@ -441,7 +467,7 @@ struct StagePart {
 // the register allocator a second live copy of the accumulators.)
 template <typename T, int KB, int NST, bool AK, bool BK, typename Issue>
 __device__ __forceinline__ void run_round(int g0, Issue& issue, const Bufs<NST>& B, Acc& acc,
-                                          int wm, int wn, int lane) {
+                                          Frags<T>& f, int wm, int wn, int lane) {
   constexpr int P = NST - 1;   // prefetch distance
 #pragma unroll
   for (int u = 0; u < NST; ++u) {
@@ -449,7 +475,7 @@ __device__ __forceinline__ void run_round(int g0, Issue& issue, const Bufs<NST>&
     wait_stages<KB, NST>(P - 1);
     stage_barrier();
     const StagePart<KB, Issue> part{issue, g0 + u + P, B.a[(u + P) % NST], B.b[(u + P) % NST]};
-    compute_stage<T, KB, AK, BK>(B.a[u], B.b[u], acc, wm, wn, lane, part);
+    compute_stage<T, KB, AK, BK>(B.a[u], B.b[u], acc, f, wm, wn, lane, part);
   }
 }
 
@@ -464,8 +490,11 @@ template <typename T, int KB, int NST, bool AK, bool BK, typename Issue>
 __device__ __forceinline__ void run_stream(int base, int n, int total, Issue&& issue,
                                            const Bufs<NST>& B, Acc& acc, int wm, int wn,
                                            int lane) {
+  Frags<T> f;
+  clear_carried(f);
   for (int g0 = base; g0 < base + n; g0 += NST)
-    run_round<T, KB, NST, AK, BK>(g0, issue, B, acc, wm, wn, lane);
+    run_round<T, KB, NST, AK, BK>(g0, issue, B, acc, f, wm, wn, lane);
+  flush_carried(acc, f);
   if (base + n >= total) wait_vmcnt<0>();
 }
 
