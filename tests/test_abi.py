@@ -37,6 +37,24 @@ def test_binding_covers_the_header():
     assert set(_lib.SIGNATURES) == set(declared_functions())
 
 
+def test_library_imports_no_allocation_copy_or_sync(lib):
+    """The library never allocates, copies or clears device memory and never waits on the host:
+    its imports from the HIP runtime are kernel launches, the launch error query and the events
+    of the benchmark timing hook (whose end call waits for its own events)."""
+    import shutil
+    import subprocess
+    import linear_cross_entropy_cce_amd as cce
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--undefined-only", cce.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    hip = {line.split()[-1].split("@")[0] for line in out.splitlines()
+           if line.split() and line.split()[-1].startswith("hip")}
+    assert "hipLaunchKernel" in hip
+    assert hip <= {"hipLaunchKernel", "hipGetLastError", "hipEventCreate", "hipEventDestroy",
+                   "hipEventRecord", "hipEventElapsedTime", "hipEventSynchronize"}, hip
+
+
 def test_status_strings(lib):
     assert lib.cce_status_string(0) == b"CCE_OK"
     assert lib.cce_status_string(3) == b"CCE_ERR_WORKSPACE_TOO_SMALL"
