@@ -428,6 +428,7 @@ def main() -> int:
     flop_fwd = 2.0 * N * V * D
     flop_bwd = 6.0 * N * V * D
     skipped, total_blocks = (int(x) for x in stats.tolist())
+    n_valid = int((d["targets"] != S.IGNORE_INDEX).sum())
     skip_frac = skipped / total_blocks if total_blocks else 0.0
     tflops = (flop_fwd + flop_bwd) / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -471,6 +472,10 @@ def main() -> int:
         "tflops_executed": (4.0 * N * V * D + 4.0 * N * V * D * (1.0 - skip_frac))
                            / (ms * 1e-3) / 1e12,
         "skip_fraction_64x64_blocks": skip_frac,
+        # tokens/s counts every token (ignored ones still cost forward work, since their LSE is
+        # returned); the same over non-ignored tokens only:
+        "n_valid_tokens": n_valid,
+        "tokens_per_s_valid": n_valid / (ms * 1e-3),
         "kernels": per_step,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
