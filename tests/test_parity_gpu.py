@@ -226,7 +226,28 @@ def _random_cases(n, seed=2024):
     return cases
 
 
-@pytest.mark.parametrize("case", _random_cases(12), ids=lambda c: c[0])
+def _wide_random_cases(n, seed=2025):
+    """Wider seeded shapes: up to 9000 tokens and 20000 vocabulary rows (several backward
+    chunks), D up to 504, logit scales up to 14 (sparse softmax)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dt = "bf16" if rng.random() < 0.7 else "f32"
+        step = 8 if dt == "bf16" else 4
+        N = int(rng.choice([rng.integers(1, 300), rng.integers(300, 3000),
+                            rng.integers(3000, 9000)]))
+        D = int(rng.integers(1, 64)) * step
+        V = int(rng.choice([rng.integers(1, 600), rng.integers(600, 9000),
+                            rng.integers(9000, 20000)]))
+        cs = float(rng.choice([1.0, 3.0, 8.0, 14.0]))
+        z = None if rng.random() < 0.3 else float(rng.choice([1.0, 1.1, 1.3]))
+        ig = float(rng.choice([0.0, 0.1, 0.5]))
+        eps = float(rng.choice([0.0, EPS, 1e-3]))
+        cases.append((f"w{i}_{dt}_{N}x{D}x{V}", N, D, V, dt, cs, z, ig, eps, 700 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(12) + _wide_random_cases(12), ids=lambda c: c[0])
 def test_random_shapes(case):
     """Seeded random shapes (ragged N, D and V, both dtypes, ignored rows, three thresholds)
     against the oracle with the same threshold, element by element."""
