@@ -333,7 +333,7 @@ def main() -> int:
     ap.add_argument("--filter-eps", type=float, default=None,
                     help="override the workload's gradient filter threshold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-tokens", type=int, default=768)
     ap.add_argument("--shards", type=int, default=0,
                     help="only time the vocabulary-sharded head emulated on one GPU with this "
                          "many shards against the unsharded step (one JSON line)")
