@@ -83,8 +83,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
   float m_run[kNB], s_run[kNB];
 #pragma unroll
   for (int i = 0; i < kNB; ++i) { m_run[i] = -INFINITY; s_run[i] = 0.f; }
-  Acc acc;
-  zero_acc(acc);
+  Acc acc;   // defined by the first stage of each vocabulary tile
 
   const int ldb = D * (int)sizeof(T);
   uint32_t off[I];  // C and E tiles share the row length, hence the offsets
@@ -161,8 +160,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
         s_run[ni] = (s_run[ni] + tile) * exp2_fast(-up);
         m_run[ni] = m + up;
       }
-#pragma unroll
-      for (int i = 0; i < 16 * kMB; ++i) acc[i >> 4][ni][i & 15] = 0.f;
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -173,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
     t_first = t * n_k;
     v_cur = (vt0 + t) * kTile;
     c_cur = C + (int64_t)v_cur * D;
-    run_stream<T, KB, NST, true, true>(t * n_k, n_k, iters, issue, B, acc, wm, wn, lane);
+    run_stream<T, KB, NST, true, true, true>(t * n_k, n_k, iters, issue, B, acc, wm, wn, lane);
     epilogue(vt0 + t);
   }
 

@@ -316,6 +316,16 @@ __device__ __forceinline__ void mma(f32x16_t& acc, const f32x4_t& a, const f32x4
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], acc, 0, 0, 0);
 }
+// The same products into a fresh accumulator: the MFMA's C operand is the constant 0, so the
+// accumulator needs no clearing before its first k-group.
+__device__ __forceinline__ void mma_fresh(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, f32x16_t{}, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_fresh(f32x16_t& acc, const f32x4_t& a, const f32x4_t& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], f32x16_t{}, 0, 0, 0);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], acc, 0, 0, 0);
+}
 
 // Pins an accumulator in the instruction order.  MFMA builtins have no side effects, so the
 // code generator may move them across loads and barriers; an (empty) volatile asm statement
@@ -350,10 +360,14 @@ __device__ __forceinline__ void mma_group(Acc& acc, const Frags<T>& f, int slot)
 // so every read of this stage's LDS buffers is complete at the next barrier (other waves then
 // refill them).  Scheduling barriers and the accumulator pins keep this order.  A stream starts
 // with zero fragments in slot 1 and ends with flush_carried().
+//
+// FIRST: the stage that opens a stream into fresh accumulators.  There is no carried k-group;
+// its MFMA slots multiply zero fragments into C = 0, which defines the accumulators, so
+// nothing has to clear them (or the carried fragments) beforehand.
 template <typename T, int KB, bool AK, bool BK, typename Part>
 __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Acc& acc,
                                               Frags<T>& f, int wm, int wn, int lane,
-                                              const Part& part) {
+                                              const Part& part, bool first = false) {
   constexpr int G = Geo<KB>::kGroups;
   static_assert(G % 2 == 0, "the last k-group of a stage lives in slot 1");
   auto read = [&](int slot, int g) {
@@ -367,23 +381,34 @@ __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Ac
   read(0, 0);
   __builtin_amdgcn_sched_barrier(0);
   // the carried k-group: MFMA j, then load j; the pins keep MFMA j after load j - 1 and before
-  // load j
-  pin(acc[0][0]);
-  mma(acc[0][0], f.a[1][0], f.b[1][0]);
-  pin(acc[0][0]);
-  __builtin_amdgcn_sched_barrier(0);
-  const auto st = part.make();
-#pragma unroll
-  for (int j = 0; j < kMB * kNB; ++j) {
-    const int mi = j / kNB, ni = j % kNB;
-    if (j > 0) {
+  // load j.  In the first stage of a fresh stream the same slots hold 0 x 0 + 0 products,
+  // which define the accumulators.
+  auto carried = [&](const bool fresh) {
+    typename Traits<T>::frag_t z{};
+    auto one = [&](int mi, int ni) {
+      if (fresh) {
+        asm volatile("" : "+v"(z));   // eight distinct products: no common subexpression
+        mma_fresh(acc[mi][ni], z, z);
+      } else {
+        pin(acc[mi][ni]);
+        mma(acc[mi][ni], f.a[1][mi], f.b[1][ni]);
+      }
       pin(acc[mi][ni]);
-      mma(acc[mi][ni], f.a[1][mi], f.b[1][ni]);
-      pin(acc[mi][ni]);
-    }
-    part.one(st, j);
+    };
+    one(0, 0);
     __builtin_amdgcn_sched_barrier(0);
-  }
+    const auto st = part.make();
+#pragma unroll
+    for (int j = 0; j < kMB * kNB; ++j) {
+      if (j > 0) one(j / kNB, j % kNB);
+      part.one(st, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if (first)
+    carried(true);
+  else
+    carried(false);
 #pragma unroll
   for (int g = 0; g + 1 < G; ++g) {
     read((g + 1) & 1, g + 1);
@@ -467,7 +492,8 @@ struct StagePart {
 // the register allocator a second live copy of the accumulators.)
 template <typename T, int KB, int NST, bool AK, bool BK, typename Issue>
 __device__ __forceinline__ void run_round(int g0, Issue& issue, const Bufs<NST>& B, Acc& acc,
-                                          Frags<T>& f, int wm, int wn, int lane) {
+                                          Frags<T>& f, int wm, int wn, int lane,
+                                          bool first = false) {
   constexpr int P = NST - 1;   // prefetch distance
 #pragma unroll
   for (int u = 0; u < NST; ++u) {
@@ -475,7 +501,7 @@ __device__ __forceinline__ void run_round(int g0, Issue& issue, const Bufs<NST>&
     wait_stages<KB, NST>(P - 1);
     stage_barrier();
     const StagePart<KB, Issue> part{issue, g0 + u + P, B.a[(u + P) % NST], B.b[(u + P) % NST]};
-    compute_stage<T, KB, AK, BK>(B.a[u], B.b[u], acc, f, wm, wn, lane, part);
+    compute_stage<T, KB, AK, BK>(B.a[u], B.b[u], acc, f, wm, wn, lane, part, first && u == 0);
   }
 }
 
@@ -486,14 +512,16 @@ __device__ __forceinline__ void run_round(int g0, Issue& issue, const Bufs<NST>&
 // issue(g) prepares stage g (for g >= total: loads of zeros) and returns a StageIssue for it.
 // At the end of the stream the zero loads are waited for, so no load into LDS is left in
 // flight.
-template <typename T, int KB, int NST, bool AK, bool BK, typename Issue>
+// FRESH: the stream defines the accumulators (their previous contents are ignored); it then
+// needs n >= NST.  Otherwise it adds to them.
+template <typename T, int KB, int NST, bool AK, bool BK, bool FRESH = false, typename Issue>
 __device__ __forceinline__ void run_stream(int base, int n, int total, Issue&& issue,
                                            const Bufs<NST>& B, Acc& acc, int wm, int wn,
                                            int lane) {
   Frags<T> f;
-  clear_carried(f);
+  if constexpr (!FRESH) clear_carried(f);
   for (int g0 = base; g0 < base + n; g0 += NST)
-    run_round<T, KB, NST, AK, BK>(g0, issue, B, acc, f, wm, wn, lane);
+    run_round<T, KB, NST, AK, BK>(g0, issue, B, acc, f, wm, wn, lane, FRESH && g0 == base);
   flush_carried(acc, f);
   if (base + n >= total) wait_vmcnt<0>();
 }
