@@ -9,8 +9,9 @@
  *     loss[n] = lse[n] - z[n, t[n]]     (0 when t[n] == ignore_index)
  *
  * and its gradients dE = G C, dC = G^T E with G[n,v] = dloss[n] (softmax[n,v] - [v == t[n]]),
- * where the backward skips gradient blocks whose softmax entries are all below filter_eps
- * (same abstract, sentence 9).  The N x V logit matrix is never materialised in device memory.
+ * where the backward skips gradient blocks whose softmax entries are all below filter_eps and
+ * drops single entries below filter_eps * 2^-8 (same abstract, sentence 9).  The N x V logit
+ * matrix is never materialised in device memory.
  *
  * Conventions shared by every call:
  *   - E and C are row-major and contiguous, of the same dtype (cce_dtype); D is the row length.
@@ -91,7 +92,9 @@ cce_status cce_forward(const void* E, const void* C, const int64_t* targets,
  *   filter_eps           gradient filtering threshold on softmax values (not scaled by dloss);
  *                        0 disables it.  A 64-token x 64-vocabulary block of G is skipped when
  *                        all of its softmax entries are < filter_eps and it holds no target of
- *                        a non-ignored row.  2^-12 is the threshold used by the benchmarks.
+ *                        a non-ignored row; in the blocks that are kept, an entry other than
+ *                        the row's target is dropped (taken as 0) when its softmax value is
+ *                        < filter_eps * 2^-8.  2^-12 is the threshold used by the benchmarks.
  *   dE [N,D], dC [V,D]   device, overwritten (no need to clear them first), in grad_dtype:
  *                        CCE_F32, or CCE_BF16 (accumulated in fp32, rounded to nearest even
  *                        once at the end; 16-byte aligned like every array argument).

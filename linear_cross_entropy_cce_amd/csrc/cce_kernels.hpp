@@ -13,7 +13,7 @@
 //   k_merge_shards  merge of per-shard LSEs and target logits into loss and LSE.
 //   k_bwd_g       recomputes S for a vocabulary chunk (tile_bwd_g), forms
 //                 G = dloss (softmax - onehot) in registers, flags negligible 64 x 64 blocks,
-//                 stores the rest of G (bf16).
+//                 drops entries below the entry floor, stores the rest of G (bf16).
 //   k_bwd_fused   per chunk c: dE (+)= G_c C_c (tile_bwd_de) and dC_c = G_c^T E (tile_bwd_dc),
 //                 skipping flagged K stages, together with tile_bwd_g of chunk c + 1.
 //   k_f32_to_bf16, k_zero_f32, k_mean, k_skip_init  small helpers (bf16 gradient output,
@@ -400,8 +400,13 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
   run_stream<T, KB, NST, true, true>(0, n_k, n_k, issue, B, acc, wm, wn, lane);
 
   // epilogue: p = 2^(z log2 e - lse log2 e); G = coef (p - [row == target]); per lane and
-  // 64 x 64 block the largest p (independent maxima, no serial chains)
+  // 64 x 64 block the largest p (independent maxima, no serial chains).  Entries with p below
+  // the entry floor eps * 2^-8 (eps scaled down by bf16's relative precision) are dropped from
+  // G, the target entry never: a subset of what dropping every non-target p < eps would drop
+  // (the CCE abstract, sentence 9).  The products over the zeros that result cost the MFMA
+  // units less power, which the board's power limit turns into clock.
   const bool filter = eps > 0.f;
+  const float p_floor = eps * (1.f / 256.f);
   const bool full = vl0 + kTile <= vc;
   if (!full) {
     // last tile of the chunk: rows at or past vc get p = 0
@@ -467,8 +472,9 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
           for (int r = 0; r < 16; ++r) {
             const float p = exp2_fast(__builtin_fmaf(acc[mi][ni][r], kLog2e, -lse2[ni]));
             pmax[ni] = fmaxf(pmax[ni], p);
+            const bool is_t = acc_row_c(mi, r) == tcmp[ni];
             acc[mi][ni][r] =
-                __builtin_fmaf(coef[ni], p, acc_row_c(mi, r) == tcmp[ni] ? -coef[ni] : 0.f);
+                __builtin_fmaf(coef[ni], p < p_floor && !is_t ? 0.f : p, is_t ? -coef[ni] : 0.f);
           }
       } else {
 #pragma unroll
@@ -477,7 +483,7 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
           for (int r = 0; r < 16; ++r) {
             const float p = exp2_fast(__builtin_fmaf(acc[mi][ni][r], kLog2e, -lse2[ni]));
             pmax[ni] = fmaxf(pmax[ni], p);
-            acc[mi][ni][r] = __builtin_fmaf(coef[ni], p, 0.f);
+            acc[mi][ni][r] = __builtin_fmaf(coef[ni], p < p_floor ? 0.f : p, 0.f);
           }
       }
     }

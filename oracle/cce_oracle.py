@@ -23,19 +23,27 @@ The pages give neither a threshold nor a granularity.  Reading used here: the to
 plane is cut into aligned blocks of block_n x block_v (64 x 64 by default, the granularity the
 GPU library reports); a block is negligible iff every valid token row n in it has
 p[n, v] < filter_eps for every v in it AND no valid row's target lies in it.  Negligible
-blocks of G are set to zero before dE and dC are formed.  filter_eps = 0 filters nothing.
-Rows whose target is ignore_index have G = 0 and do not make a block significant.
+blocks of G are set to zero before dE and dC are formed.  Inside the blocks that are kept, an
+entry whose p is below the entry floor filter_eps * 2^-8 (the threshold scaled down by bf16's
+relative precision) is set to zero too, unless it is the row's target entry: the dropped entries
+are a subset of those the element-wise reading of s9 (drop every non-target p < filter_eps)
+would drop.  filter_eps = 0 filters nothing.  Rows whose target is ignore_index have G = 0 and
+do not make a block significant.
 
 Pins: every function here is checked in tests/test_oracle.py against mpmath brute force,
 closed forms, invariants, finite differences and torch's CPU cross-entropy; the block filter
-is checked against a pure-Python loop and constructed far-away blocks.
+and the entry floor are checked against a pure-Python loop, constructed far-away blocks and a
+constructed target entry below the floor.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["logits", "forward", "backward", "loss_mean", "block_negligible", "token_rows",
-           "validate_targets"]
+__all__ = ["logits", "forward", "backward", "loss_mean", "block_negligible", "entry_negligible",
+           "token_rows", "validate_targets", "ENTRY_FLOOR"]
+
+# Entry floor relative to filter_eps: 2^-8, the relative precision of bf16 (8 significant bits).
+ENTRY_FLOOR = 2.0 ** -8
 
 
 def _f64(x):
@@ -123,6 +131,16 @@ def block_negligible(P, t_rows, valid_rows, filter_eps: float, n0: int, v0: int,
     return out
 
 
+def entry_negligible(P, t_rows, valid_rows, filter_eps: float, v0: int) -> np.ndarray:
+    """Entries of a probability sub-matrix P (columns v0..) below the entry floor
+    filter_eps * ENTRY_FLOOR, other than each valid row's target entry.  Returns bool, P's shape.
+    Rows that are not valid are never marked (their G is zero anyway)."""
+    out = (P < filter_eps * ENTRY_FLOOR) & valid_rows[:, None]
+    rows = np.nonzero(valid_rows & (t_rows >= v0) & (t_rows < v0 + P.shape[1]))[0]
+    out[rows, t_rows[rows] - v0] = False
+    return out
+
+
 def backward(E, C, targets, dloss, ignore_index: int = -100, filter_eps: float = 0.0,
              block_n: int = 64, block_v: int = 64, chunk: int = 256, vchunk: int = 65536):
     """dE [N,D] and dC [V,D] in float64, plus (negligible blocks, total blocks).
@@ -156,6 +174,7 @@ def backward(E, C, targets, dloss, ignore_index: int = -100, filter_eps: float =
             if neg.any():
                 for i, j in zip(*np.nonzero(neg)):
                     G[i * block_n:(i + 1) * block_n, j * block_v:(j + 1) * block_v] = 0.0
+            G[entry_negligible(P, tr, valid, filter_eps, v0)] = 0.0
             dE[n0:n1] += G @ C64[v0:v1]
             dC[v0:v1] += G.T @ E_rows
     total = (-(-N // block_n)) * (-(-V // block_v))
@@ -220,6 +239,7 @@ def token_rows(E, C, targets, rows, dloss_rows, ignore_index: int = -100,
             skipped += int(neg.sum())
             for i, j in zip(*np.nonzero(neg)):
                 G[i * block_n:(i + 1) * block_n, j * block_v:(j + 1) * block_v] = 0.0
+            G[entry_negligible(P, ts, vs, filter_eps, v0)] = 0.0
             dE[sel] += G @ C_part
             dC_part[v0:v1] += G.T @ E_rows[sel]
     return {"loss": loss, "lse": lse, "dE": dE, "dC_part": dC_part, "skipped": skipped}

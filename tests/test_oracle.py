@@ -213,7 +213,8 @@ def test_out_of_range_target_is_an_error():
 
 # ---------------------------------------------------------------- gradient filtering
 def brute_filtered_grads(E, C, t, w, eps, bn, bv):
-    """Plain loops: per-element p, per-block decision, then the filtered G products."""
+    """Plain loops: per-element p, per-block decision, the entry floor (eps / 256, never the
+    target entry), then the filtered G products."""
     N, V = E.shape[0], C.shape[0]
     z = [[float(np.dot(E[n], C[v])) for v in range(V)] for n in range(N)]
     G = np.zeros((N, V))
@@ -238,6 +239,10 @@ def brute_filtered_grads(E, C, t, w, eps, bn, bv):
             if not significant and eps > 0:
                 skipped += 1
                 G[i:i + bn, j:j + bv] = 0.0
+    for n in range(N):
+        for v in range(V):
+            if t[n] != II and v != t[n] and P[n, v] < eps / 256:
+                G[n, v] = 0.0
     return G @ C, G.T @ E, skipped
 
 
@@ -253,6 +258,32 @@ def test_block_filter_matches_brute_force(eps):
     np.testing.assert_allclose(dC, bC, rtol=1e-10, atol=1e-12)
     if eps == 0.02:
         assert 0 < sk < tot  # the case exercises both outcomes
+
+
+def test_entry_floor_matches_brute_force():
+    """Entries below eps / 256 inside kept blocks are dropped, except a row's target entry; the
+    case puts row 0's target at its smallest logit, far below the floor."""
+    E, C, t = rand_case(24, 16, 40, 5, scale=3.0, ignore=(9,))
+    z0 = E[0] @ C.T
+    t[0] = int(np.argmin(z0))
+    w = np.random.default_rng(25).uniform(0.5, 1.5, 16)
+    eps = 0.05
+    dE, dC, (sk, _) = oracle.backward(E, C, t, w, II, filter_eps=eps, block_n=4, block_v=8)
+    bE, bC, bsk = brute_filtered_grads(E, C, t, w, eps, 4, 8)
+    assert sk == bsk
+    np.testing.assert_allclose(dE, bE, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dC, bC, rtol=1e-10, atol=1e-12)
+    # the case exercises the rule: the target entry of row 0 lies below the floor, and kept
+    # blocks hold entries on both sides of it
+    lse = np.log(np.exp(z0 - z0.max()).sum()) + z0.max()
+    assert np.exp(z0[t[0]] - lse) < eps / 256
+    P = np.exp(E @ C.T - oracle.forward(E, C, t, II)[1][:, None])
+    neg = oracle.block_negligible(P, t, t != II, eps, 0, 0, 4, 8)
+    kept = ~np.kron(neg, np.ones((4, 8), dtype=bool))[:16, :40] & (t != II)[:, None]
+    assert (kept & (P < eps / 256)).sum() > 20 and (kept & (P >= eps / 256)).sum() > 20
+    # without the floor the result differs by more than rounding
+    nE, _, _ = brute_filtered_grads(E, C, t, w, 0.0, 4, 8)
+    assert np.linalg.norm(dE - nE) > 1e-9 * np.linalg.norm(nE)
 
 
 def test_filter_eps_zero_is_bitwise_unfiltered():

@@ -65,3 +65,17 @@ def test_mutant_filter_counts_ignored_rows(monkeypatch):
     monkeypatch.setattr(co, "block_negligible", bad)
     with pytest.raises(AssertionError):
         T.test_far_vocabulary_blocks_are_skipped_exactly()
+
+
+def test_mutant_entry_floor_drops_targets(monkeypatch):
+    def bad(P, t_rows, valid_rows, eps, v0):
+        return (P < eps * co.ENTRY_FLOOR) & valid_rows[:, None]
+    monkeypatch.setattr(co, "entry_negligible", bad)
+    with pytest.raises(AssertionError):
+        T.test_entry_floor_matches_brute_force()
+
+
+def test_mutant_entry_floor_at_the_block_threshold(monkeypatch):
+    monkeypatch.setattr(co, "ENTRY_FLOOR", 1.0)
+    with pytest.raises(AssertionError):
+        T.test_entry_floor_matches_brute_force()
