@@ -368,3 +368,24 @@ def test_ignore_index_inside_the_vocabulary():
     assert np.abs(lse.cpu().numpy() - rlse).max() <= LOSS_TOL
     assert np.all(g_loss[t == ii] == 0.0) and np.all(g_dE[t == ii] == 0.0)
     assert rel(g_dE, rE) <= GRAD_TOL and rel(dC.cpu().numpy(), rC) <= GRAD_TOL
+
+
+def test_entry_floor_matches_the_oracle_rule(monkeypatch):
+    """In fp32 (G kept in fp32) with eps = 0.1, the entries below the floor eps / 256 carry
+    enough of G (4e-3 of dE) that the GPU must match the oracle's rule closely and differ
+    clearly from the same oracle without the floor.  No block maximum lies within 1e-3 of eps,
+    so both sides skip the same 3 of 90 blocks."""
+    d = S.small_case(300, 64, 1100, "f32", 41, 3.0, 1.1, 0.1)
+    w = S.dloss_weights(41, 300)
+    eps = 0.1
+    g = gpu_run(d, "f32", w, eps)
+    E, C, t = d["E"], d["C"], d["targets"]
+    dE1, dC1, _ = oracle.backward(E, C, t, w, II, filter_eps=eps)
+    monkeypatch.setattr(oracle.cce_oracle, "ENTRY_FLOOR", 0.0)
+    dE0, dC0, _ = oracle.backward(E, C, t, w, II, filter_eps=eps)
+    eE, eC = rel(g["dE"], dE1), rel(g["dC"], dC1)
+    fE, fC = rel(dE1, dE0), rel(dC1, dC0)
+    log(f"[entry floor] gpu vs oracle dE {eE:.2e} dC {eC:.2e}; floor effect dE {fE:.2e} dC {fC:.2e}")
+    assert g["skipped"] == 3
+    assert eE < 1e-4 and eC < 1e-4
+    assert fE > 20 * eE and fC > 20 * eC
