@@ -361,9 +361,10 @@ __device__ __forceinline__ void mma_group(Acc& acc, const Frags<T>& f, int slot)
 // refill them).  Scheduling barriers and the accumulator pins keep this order.  A stream starts
 // with zero fragments in slot 1 and ends with flush_carried().
 //
-// FIRST: the stage that opens a stream into fresh accumulators.  There is no carried k-group;
-// its MFMA slots multiply zero fragments into C = 0, which defines the accumulators, so
-// nothing has to clear them (or the carried fragments) beforehand.
+// first (uniform; set only for the stage that opens a FRESH stream): there is no carried
+// k-group; its MFMA slots multiply zero fragments into C = 0, which defines the accumulators,
+// so nothing has to clear them (or the carried fragments) beforehand.  The two variants of the
+// carried slots sit behind one uniform branch per stage.
 template <typename T, int KB, bool AK, bool BK, typename Part>
 __device__ __forceinline__ void compute_stage(const char* As, const char* Bs, Acc& acc,
                                               Frags<T>& f, int wm, int wn, int lane,
