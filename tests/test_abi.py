@@ -130,6 +130,11 @@ def test_forward_validation(lib):
     assert call(args(loss=None)) == 1
     assert call(args(wsb=ok_ws - 1)) == 3
     assert call(args(N=1 << 25)) == 2
+    assert call(args(V=(1 << 24) + 1)) == 2        # beyond the kernels' limits: unsupported
+    assert call(args(D=65536 + 8)) == 2
+    assert lib.cce_forward_workspace_bytes(16, 100, 65536 + 8, 1) == 0
+    assert lib.cce_backward_workspace_bytes(16, (1 << 24) + 1, 64, 1) == 0
+    assert lib.cce_forward_workspace_bytes(16, 1 << 24, 65536, 1) > 0   # the limits themselves
     assert call(args(N=0, E=None, C=None, t=None, loss=None, lse=None, ws=None)) == 0
     for name in ("E", "C", "ws"):                      # 16-byte vectors: misaligned -> rejected
         assert call(args(**{name: ctypes.c_void_p(0x1008)})) == 1

@@ -389,3 +389,11 @@ def test_entry_floor_matches_the_oracle_rule(monkeypatch):
     assert g["skipped"] == 3
     assert eE < 1e-4 and eC < 1e-4
     assert fE > 20 * eE and fC > 20 * eC
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_largest_feature_dimension(dtype):
+    """D = 65536, the largest the kernels take: row strides of 128 / 256 KB, 1024 K stages per
+    tile, 256 dE and dC tiles along D."""
+    d = S.small_case(130, 65536, 300, dtype, 43, 3.0, 1.1, 0.1)
+    check_against_oracle(d, dtype, S.dloss_weights(43, 130), EPS, f"d65536_{dtype}")
