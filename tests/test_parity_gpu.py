@@ -397,3 +397,11 @@ def test_largest_feature_dimension(dtype):
     tile, 256 dE and dC tiles along D."""
     d = S.small_case(130, 65536, 300, dtype, 43, 3.0, 1.1, 0.1)
     check_against_oracle(d, dtype, S.dloss_weights(43, 130), EPS, f"d65536_{dtype}")
+
+
+def test_largest_vocabulary():
+    """V = 2^24, the largest the kernels take (D = 8): 65 536 vocabulary tiles, 2048 backward
+    chunks, 262 144 filter blocks.  Unfiltered, so one oracle backward suffices (~40 s)."""
+    d = S.small_case(64, 8, 1 << 24, "bf16", 44, 3.0, 1.1, 0.1)
+    g = check_against_oracle(d, "bf16", S.dloss_weights(44, 64), 0.0, "v2^24")
+    assert g["total"] == 1 * (1 << 18) and g["skipped"] == 0
