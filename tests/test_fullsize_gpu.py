@@ -82,3 +82,41 @@ def test_full_size_sampled(name, eps_override):
         assert float(s.norm() / dC.double().abs().sum(0).norm()) <= 1e-3
         assert int(stats[0]) == 0
     assert 0 <= int(stats[0]) <= int(stats[1]) == -(-N // 64) * -(-w.V // 64)
+
+
+def test_largest_batch_sampled():
+    """N = 2^24 tokens, the largest the kernels take (D = 8, V = 64): 65 536 token tiles, one
+    dC tile reducing over 262 144 stages, filter flags for 262 144 token blocks.  Sampled like
+    the benchmark sizes: two 64-token blocks against the oracle, the rest through E^T dE =
+    dC^T C."""
+    N = 1 << 24
+    d = S.small_case(N, 8, 64, "bf16", 45, 3.0, 1.1, 0.1)
+    rows = np.r_[0:64, N - 64:N]
+    E, C, t = upload(d, "bf16")
+    loss, lse = cce.cce_forward(E, C, t, II)
+    wrow = S.dloss_weights(9, len(rows))
+    dl = torch.zeros(N, dtype=torch.float32, device=DEV)
+    dl[torch.from_numpy(rows).to(DEV)] = torch.from_numpy(wrow).to(DEV)
+    stats = torch.zeros(2, dtype=torch.int64, device=DEV)
+    dE, dC = cce.cce_backward(dl, E, C, t, lse, II, S.FILTER_EPS, skip_stats=stats)
+    torch.cuda.synchronize()
+    r = oracle.token_rows(d["E"], d["C"], d["targets"], rows, wrow, II, filter_eps=S.FILTER_EPS)
+    g_loss, g_lse = loss.cpu().numpy()[rows], lse.cpu().numpy()[rows]
+    assert np.abs(g_loss - r["loss"]).max() <= LOSS_TOL
+    assert np.abs(g_lse - r["lse"]).max() <= LOSS_TOL
+    e_dE = rel(dE.cpu().numpy()[rows], r["dE"])
+    e_dC = rel(dC.cpu().numpy(), r["dC_part"])
+    log(f"[N=2^24] loss {np.abs(g_loss - r['loss']).max():.2e} dE {e_dE:.2e} dC {e_dC:.2e} "
+        f"skipped {stats.tolist()}")
+    assert e_dE <= GRAD_TOL and e_dC <= GRAD_TOL
+    assert int(stats[1]) == (N // 64) * 1
+    wfull = torch.from_numpy(S.dloss_weights(10, N)).to(DEV)
+    dE, dC = cce.cce_backward(wfull, E, C, t, lse, II, 0.0, dE=dE, dC=dC)
+    torch.cuda.synchronize()
+    lhs = E.double().T @ dE.double()
+    rhs = dC.double().T @ C.double()
+    e_id = float((lhs - rhs).norm() / rhs.norm())
+    s = dC.double().sum(0)
+    log(f"[N=2^24] E^T dE vs dC^T C {e_id:.2e}")
+    assert e_id <= 1e-3
+    assert float(s.norm() / dC.double().abs().sum(0).norm()) <= 1e-3
