@@ -362,8 +362,8 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}); "
-              "the multi-GPU sharding of the path is a design note, not a benchmark.",
+        print(f"bench.py: libcce is measured on one GPU only (asked for {max(args.gpus, world)}); "
+              "sharding the head over several GPUs is described, not benchmarked.",
               file=sys.stderr, flush=True)
         return 2
 
