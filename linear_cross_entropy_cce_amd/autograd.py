@@ -7,7 +7,7 @@ E [N,D] (token embeddings) and C [V,D] (classifier rows) are CUDA tensors of one
 fp32); targets [N] int64.  The loss of token n is lse_v(E_n . C_v) - E_n . C_t(n), 0 for ignored
 tokens (the Cut Cross-Entropy abstract, taxoreview.com page dblp:393/3562, sentences 4-6); the
 backward skips 64 x 64 blocks of the softmax gradient whose entries are all below filter_eps
-(sentence 9; 0 disables it).
+and drops single non-target entries below filter_eps * 2^-8 (sentence 9; 0 disables both).
 
 Every step of the computation runs in libcce's kernels (cce_forward / cce_backward /
 cce_loss_mean, which return the gradients in the dtype of E and C, accumulated in fp32); this
