@@ -231,9 +231,11 @@ def shards_compare(workload: str, n_shards: int, steps: int, warmup: int) -> int
     def sharded_step():
         return sharded.forward_backward(E, C, t, bounds, S.IGNORE_INDEX, w.filter_eps, dloss=dl)
 
+    tmax = cce.tile_max_buffer(E, C)
+
     def plain_step():
-        loss, lse = cce.cce_forward(E, C, t, S.IGNORE_INDEX)
-        return cce.cce_backward(dl, E, C, t, lse, S.IGNORE_INDEX, w.filter_eps)
+        loss, lse = cce.cce_forward(E, C, t, S.IGNORE_INDEX, tile_max=tmax)
+        return cce.cce_backward(dl, E, C, t, lse, S.IGNORE_INDEX, w.filter_eps, tile_max=tmax)
 
     out = {"workload": f"{w.name}: N={w.N} D={w.D} V={w.V} {w.dtype}", "shards": n_shards,
            "shard_rows": [b - a for a, b in zip(bounds, bounds[1:])]}
@@ -293,11 +295,12 @@ def vocab_order_compare(workload: str, steps: int, warmup: int) -> int:
     res = {}
     for name, CC, tt in (("as_given", C, t), ("relabelled", Cp, tp)):
         stats = torch.zeros(2, dtype=torch.int64, device=dev)
+        tmax = cce.tile_max_buffer(E, CC)
 
         def step():
-            loss, lse = cce.cce_forward(E, CC, tt, S.IGNORE_INDEX)
+            loss, lse = cce.cce_forward(E, CC, tt, S.IGNORE_INDEX, tile_max=tmax)
             dE, dC = cce.cce_backward(dl, E, CC, tt, lse, S.IGNORE_INDEX, w.filter_eps,
-                                      skip_stats=stats)
+                                      tile_max=tmax, skip_stats=stats)
             return loss, dE, dC
         for _ in range(warmup):
             step()
@@ -400,12 +403,14 @@ def main() -> int:
     bws_b = cce.backward_workspace_bytes(N, V, D, tdt)
     fws = cce._lib.workspace(fws_b, dev)
     bws = cce._lib.workspace(bws_b, dev)
+    tmax = cce.tile_max_buffer(E, C)      # the forward's tile maxima, kept for the backward
+    tmax_b = tmax.numel() * 4
     torch.cuda.reset_peak_memory_stats()
 
     def step():
-        cce.cce_forward(E, C, t, S.IGNORE_INDEX, loss=loss, lse=lse, ws=fws)
-        cce.cce_backward(dloss, E, C, t, lse, S.IGNORE_INDEX, eps, dE=dE, dC=dC, ws=bws,
-                         skip_stats=stats)
+        cce.cce_forward(E, C, t, S.IGNORE_INDEX, loss=loss, lse=lse, tile_max=tmax, ws=fws)
+        cce.cce_backward(dloss, E, C, t, lse, S.IGNORE_INDEX, eps, tile_max=tmax, dE=dE, dC=dC,
+                         ws=bws, skip_stats=stats)
 
     for _ in range(args.warmup):
         step()
@@ -480,6 +485,7 @@ def main() -> int:
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
         "extra_hbm_bytes": {"forward_workspace": fws_b, "backward_workspace": bws_b,
+                            "tile_max": tmax_b,
                             "per_token": (fws_b + bws_b) / N,
                             "allocator_peak_delta": int(peak_extra),
                             "logits_fp32_avoided": 4 * N * V},

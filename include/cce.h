@@ -63,7 +63,7 @@ const char* cce_status_string(cce_status s);
  *   backward: 2 * roundup(N,256) * Vc * sizeof(dtype): the softmax-gradient tile store of two
  *             vocabulary chunks in flight (Vc <= 8192 columns), plus their 64x64 block flags,
  *             plus N * D * 4 bytes for the fp32 dE accumulator used when the gradients are
- *             requested in bf16;
+ *             requested in bf16, plus 4 * ceil(N/256) bytes (each token tile's smallest LSE);
  *   mean    : forward + backward + 8 * roundup(N,64) + 256.
  * Returns 0 for invalid sizes. */
 size_t cce_forward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dtype);
@@ -77,18 +77,35 @@ size_t cce_loss_mean_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype 
  *                        set to 1 (if err_flag is non-NULL); read it after synchronising.
  *   loss [N], lse [N]    fp32, device, written.  lse is the natural-log LSE; it is written
  *                        for ignored rows too.
+ *   tile_max             fp32, device, NULL or cce_tile_max_count() floats (4-byte aligned),
+ *                        written: for every 256-token x 256-row tile of the logits (token tile
+ *                        i, vocabulary tile j) and each of its eight 128-row x 64-token parts
+ *                        w, the largest logit times log2(e), at [(i * ceil(V/256) + j) * 8 +
+ *                        w] (-inf where a part holds no row < V or no token < N).  Passed on
+ *                        to cce_backward, it lets the backward skip negligible tiles.
  *   ws, ws_bytes         device workspace of at least cce_forward_workspace_bytes().
  *   err_flag             device int32 or NULL; only ever set to 1, never cleared. */
 cce_status cce_forward(const void* E, const void* C, const int64_t* targets,
                        int64_t N, int64_t V, int64_t D, cce_dtype dtype, int64_t ignore_index,
-                       float* loss, float* lse, void* ws, size_t ws_bytes, int32_t* err_flag,
-                       void* stream);
+                       float* loss, float* lse, float* tile_max, void* ws, size_t ws_bytes,
+                       int32_t* err_flag, void* stream);
+
+/* Floats of cce_forward's tile_max for a problem: ceil(N/256) * ceil(V/256) * 8 (pure host;
+ * 0 for invalid sizes).  Optional output, so not part of the O(N) workspace. */
+int64_t cce_tile_max_count(int64_t N, int64_t V, int64_t D, cce_dtype dtype);
 
 /* Backward (abstract sentences 4 and 9): dE and dC of sum_n dloss[n] * loss[n].
  *   dloss                fp32, device: [N] when dloss_stride == 1, one scalar when 0.
  *   E, C, targets        as in cce_forward.  Invalid targets do not fault; their rows get no
  *                        one-hot term (the forward reports them).
  *   lse [N]              fp32, device: the lse written by cce_forward for the same E, C.
+ *   tile_max             NULL, or the tile_max written by cce_forward for the same E, C and
+ *                        targets: with filter_eps > 0, a 256 x 256 tile whose largest logit
+ *                        minus the smallest LSE of its non-ignored tokens lies below
+ *                        ln(filter_eps) (by a margin of 2^-10 in log2 units) and that holds no
+ *                        token's target is not recomputed: every block of it is negligible, and
+ *                        it is flagged and counted as such.  The results are the same as
+ *                        without tile_max.
  *   filter_eps           gradient filtering threshold on softmax values (not scaled by dloss);
  *                        0 disables it.  A 64-token x 64-vocabulary block of G is skipped when
  *                        all of its softmax entries are < filter_eps and it holds no target of
@@ -102,10 +119,10 @@ cce_status cce_forward(const void* E, const void* C, const int64_t* targets,
  *   skip_stats           device int64[2] or NULL: [0] = skipped 64x64 blocks,
  *                        [1] = all blocks, ceil(N/64) * ceil(V/64). */
 cce_status cce_backward(const float* dloss, int64_t dloss_stride, const void* E, const void* C,
-                        const int64_t* targets, const float* lse, int64_t N, int64_t V,
-                        int64_t D, cce_dtype dtype, int64_t ignore_index, float filter_eps,
-                        void* dE, void* dC, cce_dtype grad_dtype, void* ws, size_t ws_bytes,
-                        int64_t* skip_stats, void* stream);
+                        const int64_t* targets, const float* lse, const float* tile_max,
+                        int64_t N, int64_t V, int64_t D, cce_dtype dtype, int64_t ignore_index,
+                        float filter_eps, void* dE, void* dC, cce_dtype grad_dtype, void* ws,
+                        size_t ws_bytes, int64_t* skip_stats, void* stream);
 
 /* Mean-reduced convenience call: loss_mean = sum over non-ignored rows of loss / N_valid and
  * the gradients of that mean (dloss = 1 / N_valid for every row).  With N_valid == 0 the mean
@@ -130,12 +147,14 @@ cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, i
  *   lse_shard [N]     fp32, device, written: log sum over this shard's rows of exp(E C^T).
  *   target_logit [N]  fp32, device, written: E[n] . C[t[n] - vocab_offset] when the target is
  *                     one of this shard's rows (and not ignore_index), else 0.
+ *   tile_max          NULL or cce_tile_max_count(N, V, D, dtype) floats: as in cce_forward,
+ *                     over this shard's rows.
  *   ws, ws_bytes      at least cce_forward_workspace_bytes(N, V, D, dtype).
  *   Targets outside the shard are not errors here; cce_merge_shards checks them. */
 cce_status cce_forward_shard(const void* E, const void* C, const int64_t* targets, int64_t N,
                              int64_t V, int64_t D, cce_dtype dtype, int64_t ignore_index,
                              int64_t vocab_offset, float* lse_shard, float* target_logit,
-                             void* ws, size_t ws_bytes, void* stream);
+                             float* tile_max, void* ws, size_t ws_bytes, void* stream);
 
 /* cce_merge_shards: lse_shards [n_shards][N] and target_logits [n_shards][N] (fp32, device,
  * shard-major), as written by cce_forward_shard for shards that together cover [0, V_total)
@@ -148,15 +167,16 @@ cce_status cce_merge_shards(const float* lse_shards, const float* target_logits,
                             int32_t* err_flag, void* stream);
 
 /* cce_backward_shard: cce_backward for one shard.  lse [N] is the merged (full-vocabulary) LSE;
- * dC [V,D] receives this shard's rows of dC; dE [N,D] receives this shard's term of dE (the
- * shards' dE sum to the full dE).  Filter blocks are aligned to the shard's rows (64-row blocks
- * from vocab_offset).  Workspace: cce_backward_workspace_bytes(N, V, D, dtype). */
+ * tile_max is NULL or this shard's tile_max from cce_forward_shard; dC [V,D] receives this
+ * shard's rows of dC; dE [N,D] receives this shard's term of dE (the shards' dE sum to the full
+ * dE).  Filter blocks are aligned to the shard's rows (64-row blocks from vocab_offset).
+ * Workspace: cce_backward_workspace_bytes(N, V, D, dtype). */
 cce_status cce_backward_shard(const float* dloss, int64_t dloss_stride, const void* E,
                               const void* C, const int64_t* targets, const float* lse,
-                              int64_t N, int64_t V, int64_t D, cce_dtype dtype,
-                              int64_t ignore_index, int64_t vocab_offset, float filter_eps,
-                              void* dE, void* dC, cce_dtype grad_dtype, void* ws,
-                              size_t ws_bytes, int64_t* skip_stats, void* stream);
+                              const float* tile_max, int64_t N, int64_t V, int64_t D,
+                              cce_dtype dtype, int64_t ignore_index, int64_t vocab_offset,
+                              float filter_eps, void* dE, void* dC, cce_dtype grad_dtype,
+                              void* ws, size_t ws_bytes, int64_t* skip_stats, void* stream);
 
 /* Launch-shape introspection for reports (pure host): the vocabulary split count of the
  * forward and the vocabulary chunk width Vc of the backward for a problem. */

@@ -7,11 +7,12 @@ dC, computed by hand-written HIP kernels without writing the N x V logits to dev
 from ._lib import (KERNEL_KINDS, CCEError, LIB_PATH, backward_chunk, backward_workspace_bytes,
                    cce_backward, cce_backward_shard, cce_forward, cce_forward_shard,
                    cce_loss_mean, cce_merge_shards, forward_splits, forward_workspace_bytes, lib,
-                   loss_mean_workspace_bytes, timing_begin, timing_end)
+                   loss_mean_workspace_bytes, tile_max_buffer, tile_max_count, timing_begin,
+                   timing_end)
 from .autograd import LinearCrossEntropy, linear_cross_entropy
 
 __all__ = ["LinearCrossEntropy", "linear_cross_entropy", "CCEError", "LIB_PATH",
            "backward_chunk", "backward_workspace_bytes", "cce_backward", "cce_backward_shard",
            "cce_forward", "cce_forward_shard", "cce_loss_mean", "cce_merge_shards",
            "forward_splits", "forward_workspace_bytes", "lib", "loss_mean_workspace_bytes",
-           "KERNEL_KINDS", "timing_begin", "timing_end"]
+           "tile_max_buffer", "tile_max_count", "KERNEL_KINDS", "timing_begin", "timing_end"]

@@ -31,19 +31,21 @@ SIGNATURES = {
     "cce_loss_mean_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "cce_forward_splits": (_i64, [_i64, _i64, _i64, _i32]),
     "cce_backward_chunk": (_i64, [_i64, _i64, _i64, _i32]),
+    "cce_tile_max_count": (_i64, [_i64, _i64, _i64, _i32]),
     "cce_forward": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _c_ptr, _c_ptr,
-                           _c_ptr, _sz, _c_ptr, _c_ptr]),
-    "cce_backward": (_i32, [_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32,
-                            _i64, _f32, _c_ptr, _c_ptr, _i32, _c_ptr, _sz, _c_ptr, _c_ptr]),
+                           _c_ptr, _c_ptr, _sz, _c_ptr, _c_ptr]),
+    "cce_backward": (_i32, [_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i64, _i64,
+                            _i64, _i32, _i64, _f32, _c_ptr, _c_ptr, _i32, _c_ptr, _sz, _c_ptr,
+                            _c_ptr]),
     "cce_loss_mean": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _f32, _c_ptr,
                              _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _sz, _c_ptr, _c_ptr, _c_ptr]),
     "cce_forward_shard": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _i64,
-                                 _c_ptr, _c_ptr, _c_ptr, _sz, _c_ptr]),
+                                 _c_ptr, _c_ptr, _c_ptr, _c_ptr, _sz, _c_ptr]),
     "cce_merge_shards": (_i32, [_c_ptr, _c_ptr, _i64, _i64, _c_ptr, _i64, _i64, _c_ptr, _c_ptr,
                                 _c_ptr, _c_ptr]),
-    "cce_backward_shard": (_i32, [_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64,
-                                  _i32, _i64, _i64, _f32, _c_ptr, _c_ptr, _i32, _c_ptr, _sz,
-                                  _c_ptr, _c_ptr]),
+    "cce_backward_shard": (_i32, [_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i64,
+                                  _i64, _i64, _i32, _i64, _i64, _f32, _c_ptr, _c_ptr, _i32,
+                                  _c_ptr, _sz, _c_ptr, _c_ptr]),
     "cce_timing_begin": (_i32, [ctypes.c_uint32, ctypes.c_int32]),
     "cce_timing_end": (_i32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int64)]),
 }
@@ -143,21 +145,45 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def cce_forward(E, C, targets, ignore_index: int = -100, *, loss=None, lse=None, ws=None,
-                err_flag=None, stream=None):
-    """Per-token loss and LSE (fp32 [N]).  Returns (loss, lse)."""
+def tile_max_count(N: int, V: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().cce_tile_max_count(N, V, D, dtype_code(dtype)))
+
+
+def tile_max_buffer(E, C) -> torch.Tensor:
+    """An fp32 device buffer for the forward's tile maxima (cce_forward(tile_max=...)), to be
+    passed on to cce_backward(tile_max=...)."""
+    n = tile_max_count(E.shape[0], C.shape[0], E.shape[1], E.dtype)
+    return torch.empty(max(n, 1), dtype=torch.float32, device=E.device)
+
+
+def _check_tile_max(t, N, V, D, dt, dev):
+    if t is None:
+        return
+    n = int(lib().cce_tile_max_count(N, V, D, dt))
+    if (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda or t.device != dev
+            or t.numel() < n):
+        raise ValueError(f"tile_max must be a contiguous float32 tensor of at least {n} "
+                         f"elements on {dev}")
+
+
+def cce_forward(E, C, targets, ignore_index: int = -100, *, loss=None, lse=None, tile_max=None,
+                ws=None, err_flag=None, stream=None):
+    """Per-token loss and LSE (fp32 [N]).  Returns (loss, lse).  tile_max (optional, from
+    tile_max_buffer) receives the tile maxima that let cce_backward skip negligible tiles."""
     N, V, D, dt = _check_inputs(E, C, targets)
     dev = E.device
     loss = torch.empty(N, dtype=torch.float32, device=dev) if loss is None else loss
     lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else lse
     _check_vec("loss", loss, N, torch.float32, dev)
     _check_vec("lse", lse, N, torch.float32, dev)
+    _check_tile_max(tile_max, N, V, D, dt, dev)
     need = lib().cce_forward_workspace_bytes(N, V, D, dt)
     ws = workspace(need, dev) if ws is None else ws
     with torch.cuda.device(dev):
         _check("cce_forward", lib().cce_forward(
             _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, _ptr(loss), _ptr(lse),
-            _ptr(ws), ws.numel() * ws.element_size(), _ptr(err_flag), _stream(stream)))
+            _ptr(tile_max), _ptr(ws), ws.numel() * ws.element_size(), _ptr(err_flag),
+            _stream(stream)))
     return loss, lse
 
 
@@ -172,9 +198,11 @@ def _grad_outputs(N, V, D, dev, grad_dtype, dE, dC):
 
 
 def cce_backward(dloss, E, C, targets, lse, ignore_index: int = -100, filter_eps: float = 0.0,
-                 *, dE=None, dC=None, grad_dtype=None, ws=None, skip_stats=None, stream=None):
+                 *, tile_max=None, dE=None, dC=None, grad_dtype=None, ws=None, skip_stats=None,
+                 stream=None):
     """dE [N,D] and dC [V,D] in grad_dtype (torch.float32 by default, or torch.bfloat16).
-    dloss: fp32 [N], or a 1-element tensor (scalar)."""
+    dloss: fp32 [N], or a 1-element tensor (scalar).  tile_max: the forward's tile maxima for
+    the same E, C and targets, or None."""
     N, V, D, dt = _check_inputs(E, C, targets)
     dev = E.device
     if dloss.dtype != torch.float32 or not dloss.is_cuda:
@@ -183,13 +211,14 @@ def cce_backward(dloss, E, C, targets, lse, ignore_index: int = -100, filter_eps
     if stride == 1 and dloss.shape != (N,):
         raise ValueError("dloss must have N elements or one")
     _check_vec("lse", lse, N, torch.float32, dev)
+    _check_tile_max(tile_max, N, V, D, dt, dev)
     dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
     need = lib().cce_backward_workspace_bytes(N, V, D, dt)
     ws = workspace(need, dev) if ws is None else ws
     with torch.cuda.device(dev):
         _check("cce_backward", lib().cce_backward(
-            _ptr(dloss), stride, _ptr(E), _ptr(C), _ptr(targets), _ptr(lse), N, V, D, dt,
-            ignore_index, float(filter_eps), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
+            _ptr(dloss), stride, _ptr(E), _ptr(C), _ptr(targets), _ptr(lse), _ptr(tile_max), N,
+            V, D, dt, ignore_index, float(filter_eps), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
             ws.numel() * ws.element_size(), _ptr(skip_stats), _stream(stream)))
     return dE, dC
 
@@ -215,7 +244,7 @@ def cce_loss_mean(E, C, targets, ignore_index: int = -100, filter_eps: float = 0
 
 
 def cce_forward_shard(E, C_shard, targets, vocab_offset: int, ignore_index: int = -100, *,
-                      lse=None, target_logit=None, ws=None, stream=None):
+                      lse=None, target_logit=None, tile_max=None, ws=None, stream=None):
     """One vocabulary shard's forward: (lse over the shard's rows, target logit or 0), fp32 [N].
     targets index the full vocabulary; C_shard holds rows [vocab_offset, vocab_offset + V)."""
     N, V, D, dt = _check_inputs(E, C_shard, targets)
@@ -224,12 +253,14 @@ def cce_forward_shard(E, C_shard, targets, vocab_offset: int, ignore_index: int 
     zt = torch.empty(N, dtype=torch.float32, device=dev) if target_logit is None else target_logit
     _check_vec("lse", lse, N, torch.float32, dev)
     _check_vec("target_logit", zt, N, torch.float32, dev)
+    _check_tile_max(tile_max, N, V, D, dt, dev)
     need = lib().cce_forward_workspace_bytes(N, V, D, dt)
     ws = workspace(need, dev) if ws is None else ws
     with torch.cuda.device(dev):
         _check("cce_forward_shard", lib().cce_forward_shard(
             _ptr(E), _ptr(C_shard), _ptr(targets), N, V, D, dt, ignore_index, int(vocab_offset),
-            _ptr(lse), _ptr(zt), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+            _ptr(lse), _ptr(zt), _ptr(tile_max), _ptr(ws), ws.numel() * ws.element_size(),
+            _stream(stream)))
     return lse, zt
 
 
@@ -255,8 +286,8 @@ def cce_merge_shards(lse_shards, target_logits, targets, V_total: int, ignore_in
 
 
 def cce_backward_shard(dloss, E, C_shard, targets, lse, vocab_offset: int,
-                       ignore_index: int = -100, filter_eps: float = 0.0, *, dE=None, dC=None,
-                       grad_dtype=None, ws=None, skip_stats=None, stream=None):
+                       ignore_index: int = -100, filter_eps: float = 0.0, *, tile_max=None,
+                       dE=None, dC=None, grad_dtype=None, ws=None, skip_stats=None, stream=None):
     """One vocabulary shard's backward with the merged LSE: (this shard's term of dE, the
     shard's rows of dC)."""
     N, V, D, dt = _check_inputs(E, C_shard, targets)
@@ -267,14 +298,16 @@ def cce_backward_shard(dloss, E, C_shard, targets, lse, vocab_offset: int,
     if stride == 1 and dloss.shape != (N,):
         raise ValueError("dloss must have N elements or one")
     _check_vec("lse", lse, N, torch.float32, dev)
+    _check_tile_max(tile_max, N, V, D, dt, dev)
     dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
     need = lib().cce_backward_workspace_bytes(N, V, D, dt)
     ws = workspace(need, dev) if ws is None else ws
     with torch.cuda.device(dev):
         _check("cce_backward_shard", lib().cce_backward_shard(
-            _ptr(dloss), stride, _ptr(E), _ptr(C_shard), _ptr(targets), _ptr(lse), N, V, D, dt,
-            ignore_index, int(vocab_offset), float(filter_eps), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
-            ws.numel() * ws.element_size(), _ptr(skip_stats), _stream(stream)))
+            _ptr(dloss), stride, _ptr(E), _ptr(C_shard), _ptr(targets), _ptr(lse),
+            _ptr(tile_max), N, V, D, dt, ignore_index, int(vocab_offset), float(filter_eps),
+            _ptr(dE), _ptr(dC), gcode, _ptr(ws), ws.numel() * ws.element_size(),
+            _ptr(skip_stats), _stream(stream)))
     return dE, dC
 
 

@@ -51,6 +51,7 @@ bool sizes_ok(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
 }
 // The kernels move E, C, the gradients and the workspace in 16-byte vectors.
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3) == 0; }
 bool all_aligned16(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
     if (!aligned16(p)) return false;
@@ -99,10 +100,11 @@ int64_t plan_chunk(int64_t V) {
 }
 
 // Backward workspace: G and flags of two chunks in flight (c and c + 1), then the fp32 dE
-// accumulator used when the gradients are requested in bf16.
+// accumulator used when the gradients are requested in bf16, then the smallest lse log2(e) of
+// each token tile (for skipping tiles with the forward's tile maxima).
 struct BwdLayout {
   int64_t n_pad, vc, fstride;
-  size_t g_bytes, flag_bytes, acc_offset, acc_bytes, total;
+  size_t g_bytes, flag_bytes, acc_offset, acc_bytes, tmin_offset, tmin_bytes, total;
 };
 BwdLayout bwd_layout(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
   BwdLayout L;
@@ -113,7 +115,9 @@ BwdLayout bwd_layout(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
   L.flag_bytes = align_up((size_t)(L.n_pad / 64) * (size_t)L.fstride);
   L.acc_offset = 2 * (L.g_bytes + L.flag_bytes);
   L.acc_bytes = align_up((size_t)std::max<int64_t>(N, 1) * (size_t)D * 4);
-  L.total = L.acc_offset + L.acc_bytes;
+  L.tmin_offset = L.acc_offset + L.acc_bytes;
+  L.tmin_bytes = align_up((size_t)(L.n_pad / kTile) * 4);
+  L.total = L.tmin_offset + L.tmin_bytes;
   return L;
 }
 size_t fwd_bytes(int64_t N, int64_t V) {
@@ -163,10 +167,16 @@ bool k_tail(int64_t D) {
   return D % ((int64_t)kNST * kKB / (int64_t)sizeof(T)) != 0;
 }
 
+// Floats of the forward's tile maxima: one per wave of every 256 x 256 (token, vocabulary) tile.
+int64_t tile_max_count(int64_t N, int64_t V) {
+  return ceil_div(std::max<int64_t>(N, 1), kTile) * ceil_div(V, kTile) * kWaves;
+}
+
 template <typename T>
 cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, int64_t V,
-                        int64_t D, int64_t ii, float* loss, float* lse, void* ws, int32_t* err,
-                        hipStream_t st, int64_t voff = 0, float* zt = nullptr) {
+                        int64_t D, int64_t ii, float* loss, float* lse, float* tile_max,
+                        void* ws, int32_t* err, hipStream_t st, int64_t voff = 0,
+                        float* zt = nullptr) {
   const int64_t n_split = plan_splits(N, V);
   const int64_t n_tb = ceil_div(N, kTile), n_vt = ceil_div(V, kTile);
   const int64_t items = n_tb * n_split;
@@ -175,10 +185,12 @@ cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, i
     TimedLaunch tl(CCE_KERNEL_FWD_LSE, st);
     if (k_tail<T>(D))
       hipLaunchKernelGGL((k_fwd_lse<T, kKB, kNST, true>), dim3(grid_for(items)), dim3(kThreads), 0,
-                         st, E, C, (int)N, (int)V, (int)D, (int)n_split, (int)n_vt, (int)items, part);
+                         st, E, C, (int)N, (int)V, (int)D, (int)n_split, (int)n_vt, (int)items, part,
+                         tile_max);
     else
       hipLaunchKernelGGL((k_fwd_lse<T, kKB, kNST, false>), dim3(grid_for(items)), dim3(kThreads), 0,
-                         st, E, C, (int)N, (int)V, (int)D, (int)n_split, (int)n_vt, (int)items, part);
+                         st, E, C, (int)N, (int)V, (int)D, (int)n_split, (int)n_vt, (int)items, part,
+                         tile_max);
   }
   if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   TimedLaunch tl(CCE_KERNEL_FWD_FINISH, st);
@@ -190,7 +202,8 @@ cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, i
 
 template <typename T>
 cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const T* C,
-                         const int64_t* tgt, const float* lse, int64_t N, int64_t V, int64_t D,
+                         const int64_t* tgt, const float* lse, const float* tile_max, int64_t N,
+                         int64_t V, int64_t D,
                          int64_t ii, int64_t voff, float eps, void* dE, void* dC, cce_dtype gdt,
                          void* ws, int64_t* skip_stats, hipStream_t st, cce_dtype dt) {
   const BwdLayout L = bwd_layout(N, V, D, dt);
@@ -202,6 +215,14 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
     TimedLaunch tl(CCE_KERNEL_AUX, st);
     hipLaunchKernelGGL(k_skip_init, dim3(1), dim3(64), 0, st, skip_stats,
                        ceil_div(N, 64) * ceil_div(V, 64));
+    if (launch_status() != CCE_OK) return CCE_ERR_HIP;
+  }
+  float* tile_lse_min = (float*)((char*)ws + L.tmin_offset);
+  const bool tile_skip = tile_max != nullptr && eps > 0.f;
+  if (tile_skip) {
+    TimedLaunch tl(CCE_KERNEL_AUX, st);
+    hipLaunchKernelGGL(k_tile_lse_min, dim3((unsigned)n_tb), dim3(256), 0, st, lse, tgt, (int)N,
+                       ii, tile_lse_min);
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   }
   // chunk c uses G / flag buffer c % 2
@@ -221,6 +242,13 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
     A.skip_count = (unsigned long long*)skip_stats;
     A.dE = dE_acc; A.dC = dC; A.dc_bf16 = gdt == CCE_BF16 ? 1 : 0;
     A.accumulate = c > 0 ? 1 : 0;
+    // without maxima, both pointers lead to the token-tile minima (at least 256 bytes) and the
+    // kernel reads their first floats only
+    A.tile_max = tile_skip ? tile_max : tile_lse_min;
+    A.tile_lse_min = tile_lse_min;
+    A.tile_skip = tile_skip ? 1 : 0;
+    A.n_vt_all = (int)ceil_div(V, kTile);
+    A.skip_bound = eps > 0.f ? std::log2(eps) - 1.f / 1024.f : -INFINITY;
     return A;
   };
   {
@@ -285,6 +313,11 @@ size_t cce_backward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype d
   return bwd_layout(N, V, D, dt).total;
 }
 
+int64_t cce_tile_max_count(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
+  if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
+  return tile_max_count(N, V);
+}
+
 size_t cce_loss_mean_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
   if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
   return fwd_bytes(N, V) + bwd_layout(N, V, D, dt).total + mean_extra_bytes(N);
@@ -302,19 +335,20 @@ int64_t cce_backward_chunk(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
 
 cce_status cce_forward(const void* E, const void* C, const int64_t* targets, int64_t N,
                        int64_t V, int64_t D, cce_dtype dt, int64_t ignore_index, float* loss,
-                       float* lse, void* ws, size_t ws_bytes, int32_t* err_flag, void* stream) {
+                       float* lse, float* tile_max, void* ws, size_t ws_bytes, int32_t* err_flag,
+                       void* stream) {
   if (!sizes_ok(N, V, D, dt)) return CCE_ERR_INVALID_ARGUMENT;
   if (!sizes_supported(N, V, D)) return CCE_ERR_UNSUPPORTED;
   if (N == 0) return CCE_OK;
   if (!E || !C || !targets || !loss || !lse || !ws) return CCE_ERR_INVALID_ARGUMENT;
-  if (!all_aligned16({E, C, ws})) return CCE_ERR_INVALID_ARGUMENT;
+  if (!all_aligned16({E, C, ws}) || !aligned4(tile_max)) return CCE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < fwd_bytes(N, V)) return CCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   if (dt == CCE_BF16)
     return forward_impl<__bf16>((const __bf16*)E, (const __bf16*)C, targets, N, V, D,
-                                ignore_index, loss, lse, ws, err_flag, st);
+                                ignore_index, loss, lse, tile_max, ws, err_flag, st);
   return forward_impl<float>((const float*)E, (const float*)C, targets, N, V, D, ignore_index,
-                             loss, lse, ws, err_flag, st);
+                             loss, lse, tile_max, ws, err_flag, st);
 }
 
 }  // extern "C"
@@ -323,8 +357,9 @@ namespace {
 
 // cce_backward and cce_backward_shard: vocabulary rows [voff, voff + V) in C.
 cce_status backward_entry(const float* dloss, int64_t dloss_stride, const void* E,
-                          const void* C, const int64_t* targets, const float* lse, int64_t N,
-                          int64_t V, int64_t D, cce_dtype dt, int64_t ignore_index,
+                          const void* C, const int64_t* targets, const float* lse,
+                          const float* tile_max, int64_t N, int64_t V, int64_t D, cce_dtype dt,
+                          int64_t ignore_index,
                           int64_t voff, float filter_eps, void* dE, void* dC,
                           cce_dtype grad_dtype, void* ws, size_t ws_bytes, int64_t* skip_stats,
                           void* stream) {
@@ -350,16 +385,16 @@ cce_status backward_entry(const float* dloss, int64_t dloss_stride, const void* 
   }
   if (!dloss || !E || !C || !targets || !lse || !dE || !dC || !ws)
     return CCE_ERR_INVALID_ARGUMENT;
-  if (!all_aligned16({E, C, dE, dC, ws})) return CCE_ERR_INVALID_ARGUMENT;
+  if (!all_aligned16({E, C, dE, dC, ws}) || !aligned4(tile_max)) return CCE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < bwd_layout(N, V, D, dt).total) return CCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   if (dt == CCE_BF16)
     return backward_impl<__bf16>(dloss, dloss_stride, (const __bf16*)E, (const __bf16*)C,
-                                 targets, lse, N, V, D, ignore_index, voff, filter_eps, dE, dC,
-                                 grad_dtype, ws, skip_stats, st, dt);
+                                 targets, lse, tile_max, N, V, D, ignore_index, voff,
+                                 filter_eps, dE, dC, grad_dtype, ws, skip_stats, st, dt);
   return backward_impl<float>(dloss, dloss_stride, (const float*)E, (const float*)C, targets,
-                              lse, N, V, D, ignore_index, voff, filter_eps, dE, dC, grad_dtype,
-                              ws, skip_stats, st, dt);
+                              lse, tile_max, N, V, D, ignore_index, voff, filter_eps, dE, dC,
+                              grad_dtype, ws, skip_stats, st, dt);
 }
 
 }  // namespace
@@ -367,44 +402,46 @@ cce_status backward_entry(const float* dloss, int64_t dloss_stride, const void* 
 extern "C" {
 
 cce_status cce_backward(const float* dloss, int64_t dloss_stride, const void* E, const void* C,
-                        const int64_t* targets, const float* lse, int64_t N, int64_t V,
-                        int64_t D, cce_dtype dt, int64_t ignore_index, float filter_eps,
-                        void* dE, void* dC, cce_dtype grad_dtype, void* ws, size_t ws_bytes,
-                        int64_t* skip_stats, void* stream) {
-  return backward_entry(dloss, dloss_stride, E, C, targets, lse, N, V, D, dt, ignore_index, 0,
-                        filter_eps, dE, dC, grad_dtype, ws, ws_bytes, skip_stats, stream);
+                        const int64_t* targets, const float* lse, const float* tile_max,
+                        int64_t N, int64_t V, int64_t D, cce_dtype dt, int64_t ignore_index,
+                        float filter_eps, void* dE, void* dC, cce_dtype grad_dtype, void* ws,
+                        size_t ws_bytes, int64_t* skip_stats, void* stream) {
+  return backward_entry(dloss, dloss_stride, E, C, targets, lse, tile_max, N, V, D, dt,
+                        ignore_index, 0, filter_eps, dE, dC, grad_dtype, ws, ws_bytes,
+                        skip_stats, stream);
 }
 
 cce_status cce_backward_shard(const float* dloss, int64_t dloss_stride, const void* E,
                               const void* C, const int64_t* targets, const float* lse,
-                              int64_t N, int64_t V, int64_t D, cce_dtype dt,
-                              int64_t ignore_index, int64_t vocab_offset, float filter_eps,
-                              void* dE, void* dC, cce_dtype grad_dtype, void* ws,
-                              size_t ws_bytes, int64_t* skip_stats, void* stream) {
-  return backward_entry(dloss, dloss_stride, E, C, targets, lse, N, V, D, dt, ignore_index,
-                        vocab_offset, filter_eps, dE, dC, grad_dtype, ws, ws_bytes, skip_stats,
-                        stream);
+                              const float* tile_max, int64_t N, int64_t V, int64_t D,
+                              cce_dtype dt, int64_t ignore_index, int64_t vocab_offset,
+                              float filter_eps, void* dE, void* dC, cce_dtype grad_dtype,
+                              void* ws, size_t ws_bytes, int64_t* skip_stats, void* stream) {
+  return backward_entry(dloss, dloss_stride, E, C, targets, lse, tile_max, N, V, D, dt,
+                        ignore_index, vocab_offset, filter_eps, dE, dC, grad_dtype, ws, ws_bytes,
+                        skip_stats, stream);
 }
 
 cce_status cce_forward_shard(const void* E, const void* C, const int64_t* targets, int64_t N,
                              int64_t V, int64_t D, cce_dtype dt, int64_t ignore_index,
                              int64_t vocab_offset, float* lse_shard, float* target_logit,
-                             void* ws, size_t ws_bytes, void* stream) {
+                             float* tile_max, void* ws, size_t ws_bytes, void* stream) {
   if (!sizes_ok(N, V, D, dt)) return CCE_ERR_INVALID_ARGUMENT;
   if (!sizes_supported(N, V, D)) return CCE_ERR_UNSUPPORTED;
   if (vocab_offset < 0) return CCE_ERR_INVALID_ARGUMENT;
   if (N == 0) return CCE_OK;
   if (!E || !C || !targets || !lse_shard || !target_logit || !ws)
     return CCE_ERR_INVALID_ARGUMENT;
-  if (!all_aligned16({E, C, ws})) return CCE_ERR_INVALID_ARGUMENT;
+  if (!all_aligned16({E, C, ws}) || !aligned4(tile_max)) return CCE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < fwd_bytes(N, V)) return CCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   if (dt == CCE_BF16)
     return forward_impl<__bf16>((const __bf16*)E, (const __bf16*)C, targets, N, V, D,
-                                ignore_index, nullptr, lse_shard, ws, nullptr, st, vocab_offset,
-                                target_logit);
+                                ignore_index, nullptr, lse_shard, tile_max, ws, nullptr, st,
+                                vocab_offset, target_logit);
   return forward_impl<float>((const float*)E, (const float*)C, targets, N, V, D, ignore_index,
-                             nullptr, lse_shard, ws, nullptr, st, vocab_offset, target_logit);
+                             nullptr, lse_shard, tile_max, ws, nullptr, st, vocab_offset,
+                             target_logit);
 }
 
 cce_status cce_merge_shards(const float* lse_shards, const float* target_logits,
@@ -449,11 +486,11 @@ cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, i
     hipLaunchKernelGGL(k_mean, dim3(1), dim3(1024), 0, st, (const float*)nullptr,
                        (const int64_t*)nullptr, 0, ignore_index, loss_mean, dloss, n_valid);
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
-    return cce_backward(dloss, 0, E, C, targets, lse, 0, V, D, dt, ignore_index, filter_eps,
-                        dE, dC, grad_dtype, base + fb, bb, skip_stats, stream);
+    return cce_backward(dloss, 0, E, C, targets, lse, nullptr, 0, V, D, dt, ignore_index,
+                        filter_eps, dE, dC, grad_dtype, base + fb, bb, skip_stats, stream);
   }
-  cce_status s = cce_forward(E, C, targets, N, V, D, dt, ignore_index, loss, lse, base, fb,
-                             err_flag, stream);
+  cce_status s = cce_forward(E, C, targets, N, V, D, dt, ignore_index, loss, lse, nullptr, base,
+                             fb, err_flag, stream);
   if (s != CCE_OK) return s;
   {
     TimedLaunch tl(CCE_KERNEL_AUX, st);
@@ -461,8 +498,8 @@ cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, i
                        loss_mean, dloss, n_valid);
   }
   if (launch_status() != CCE_OK) return CCE_ERR_HIP;
-  return cce_backward(dloss, 0, E, C, targets, lse, N, V, D, dt, ignore_index, filter_eps, dE,
-                      dC, grad_dtype, base + fb, bb, skip_stats, stream);
+  return cce_backward(dloss, 0, E, C, targets, lse, nullptr, N, V, D, dt, ignore_index,
+                      filter_eps, dE, dC, grad_dtype, base + fb, bb, skip_stats, stream);
 }
 
 cce_status cce_timing_begin(uint32_t kind_mask, int32_t max_launches) {

@@ -53,9 +53,28 @@ __host__ __device__ constexpr int padded_stages(int K) {
   return (n + NST - 1) / NST * NST;
 }
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+
 // ------------------------------------------------------------------------------------------
 // Forward: per (token tile, vocabulary range) partial log-sum-exp in base 2.
 //   part[split * N + n] = (m, s): m = max_v z*log2(e) over the range, s = sum 2^(z*log2(e) - m)
+// Optionally (tile_max != nullptr) the largest z*log2(e) of each wave's 128 x 64 part of every
+// 256 x 256 tile, tile_max[((token tile) * n_vt + vocabulary tile) * 8 + wave], for the backward
+// to prove whole tiles negligible without recomputing them (tokens at or past N excluded).
 // ------------------------------------------------------------------------------------------
 // KT: D is not a multiple of NST stages of K, so the stages at the end of a row need the
 // per-lane K mask (the common shapes compile without it).
@@ -63,7 +82,8 @@ template <typename T, int KB, int NST, bool KT>
 __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E,
                                                          const T* __restrict__ C, int N, int V,
                                                          int D, int n_split, int n_vt,
-                                                         int n_items, float2* __restrict__ part) {
+                                                         int n_items, float2* __restrict__ part,
+                                                         float* __restrict__ tile_max) {
   CCE_STAGE_BUFFERS(KB, NST, B)
   __shared__ float2 sRed[4][kWaveN];
   constexpr int KS = KB / (int)sizeof(T);
@@ -124,9 +144,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
           for (int r = 0; r < 16; ++r)
             if (acc_row_c(mi, r) >= lim) acc[mi][ni][r] = -INFINITY;
     }
+    float zmax = -INFINITY;   // largest z log2(e) of the wave's valid token columns
 #pragma unroll
     for (int ni = 0; ni < kNB; ++ni) {
       const float m = m_run[ni];
+      const bool col_ok = tok0 + kWaveN * wn + 32 * ni + (lane & 31) < N;
       float ps[8], pm[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) { ps[k] = 0.f; pm[k] = -INFINITY; }
@@ -146,6 +168,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
         for (int i = 0; i < 16 * kMB; ++i) mx = fmaxf(mx, acc[i >> 4][ni][i & 15]);
         const float m_new = fmaxf(m, mx * kLog2e);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        if (col_ok) zmax = fmaxf(zmax, mx * kLog2e);
 #pragma unroll
         for (int k = 0; k < 8; ++k) ps[k] = 0.f;
 #pragma unroll
@@ -159,8 +182,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
         const float up = fmaxf(tmax, 0.f);       // rebase so that s stays O(number of terms)
         s_run[ni] = (s_run[ni] + tile) * exp2_fast(-up);
         m_run[ni] = m + up;
+        if (col_ok) zmax = fmaxf(zmax, tmax + m);
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (tile_max) {
+      zmax = wave_max(zmax);
+      if (lane == 0) tile_max[((int64_t)tb * n_vt + vt) * kWaves + wave] = zmax;
     }
   };
 
@@ -203,16 +231,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_lse(const T* __restrict__ E
   }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
 
 // ------------------------------------------------------------------------------------------
 // Forward finish: one wave per token.  LSE = ln2 * (M + log2 sum_i s_i 2^(m_i - M)); the
@@ -325,6 +343,11 @@ struct BwdArgs {
   void* dC;                   // [V, D] in the gradient dtype
   int dc_bf16;                // dC written as bf16 (else fp32)
   int accumulate;             // dE += (later chunks) instead of dE = (first chunk)
+  const float* tile_max;      // the forward's tile maxima (k_fwd_lse); readable when unused
+  const float* tile_lse_min;  // [n_tb] smallest lse log2(e) of each token tile (k_tile_lse_min)
+  int tile_skip;              // 1: skip tiles that tile_max proves negligible
+  int n_vt_all;               // vocabulary tiles of C (index of tile_max)
+  float skip_bound;           // log2(eps) less a margin: tiles below it are not recomputed
 };
 
 template <typename T, int KB, int NST, bool KT>
@@ -396,7 +419,54 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
     trow[ni] = tr;
   }
 
+  // With the forward's tile maxima: if max z log2(e) over the tile, less the smallest
+  // lse log2(e) of its non-ignored tokens, is below log2(eps) (by a margin that covers the
+  // rounding of both sides), every p of the tile is below eps, and if no token of the tile has
+  // its target among the tile's rows, every block of it is negligible.  The recompute is then
+  // skipped and the blocks are flagged as the epilogue would flag them.  The two bounds are
+  // read through the constant address space (scalar loads, counted apart from the stage
+  // loads), so their latency overlaps the first stage's.
+  // The loads are unconditional (without maxima both pointers lead to 256 readable bytes and
+  // the offsets are 0), so no branch makes the compiler wait for them before the stage loads.
+  typedef const __attribute__((address_space(4))) float* cfloat_p;
+  const int on = A.tile_skip;
+  const cfloat_p tm =
+      (cfloat_p)A.tile_max + ((int64_t)tb * A.n_vt_all + ((v0 + vl0) >> 8)) * kWaves * on;
+  float tmv[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) tmv[w] = tm[w];
+  const float lmin = ((cfloat_p)A.tile_lse_min)[tb * on];
   run_prologue<KB, NST>(n_k, issue, B);
+  float zt = -INFINITY;   // taken after the stage loads are issued, so they wait for nothing
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) zt = fmaxf(zt, tmv[w]);
+  if (on && zt - lmin < A.skip_bound) {
+    // every p of the tile is below eps; skip it unless a token's target lies in its rows
+    __shared__ int sHasTarget[kWaves];
+    bool here = false;
+#pragma unroll
+    for (int ni = 0; ni < kNB; ++ni) here |= trow[ni] >= 0;
+    const bool any_t = __ballot(here) != 0ull;
+    if (lane == 0) sHasTarget[wave] = any_t ? 1 : 0;
+    __syncthreads();
+    int has_t = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) has_t |= sHasTarget[w];
+    if (!has_t) {
+      wait_vmcnt<0>();   // the first stage's loads land before the workgroup ends
+      const int nblk = tok0 + kWaveN * wn;
+      int n_skipped = 0;
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int vblk = vl0 + kWaveM * wm + 64 * a;
+        if (vblk < vc && nblk < N) ++n_skipped;
+        if (lane == 0) flags[(int64_t)(nblk >> 6) * fstride + (vblk >> 6)] = 1;
+      }
+      if (skip_count && lane == 0 && n_skipped)
+        atomicAdd(skip_count, (unsigned long long)n_skipped);
+      return;
+    }
+  }
   run_stream<T, KB, NST, true, true>(0, n_k, n_k, issue, B, acc, wm, wn, lane);
 
   // epilogue: p = 2^(z log2 e - lse log2 e); G = coef (p - [row == target]); per lane and
@@ -901,6 +971,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_fused(BwdArgs<T> A, BwdArgs
     const int n = (int)gridDim.x - r_de - r_dc;
     tile_bwd_g<T, KB, NST, KT>(next, xcd_remap(b - r_de - r_dc, n), B);
   }
+}
+
+// Smallest lse log2(e) over the non-ignored tokens of each 256-token tile (+inf if none): the
+// token side of the backward's bound for skipping tiles.  One workgroup per token tile.
+__global__ __launch_bounds__(256) void k_tile_lse_min(const float* __restrict__ lse,
+                                                      const int64_t* __restrict__ tgt, int N,
+                                                      int64_t ignore_index,
+                                                      float* __restrict__ out) {
+  __shared__ float s[4];
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  float v = INFINITY;
+  if (n < N && tgt[n] != ignore_index) v = lse[n] * kLog2e;
+  v = wave_min(v);
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = fminf(fminf(s[0], s[1]), fminf(s[2], s[3]));
 }
 
 // p[0..n) = 0 (a kernel rather than a memset, so the call stays safe under graph capture)

@@ -41,10 +41,12 @@ def forward_backward(E, C, targets, bounds, ignore_index: int = -100, filter_eps
     dev = E.device
     lse_s = torch.empty((S, N), dtype=torch.float32, device=dev)
     zt_s = torch.empty((S, N), dtype=torch.float32, device=dev)
+    tmax_s = []                          # each shard keeps its tile maxima for its backward
     for s in range(S):
         v0, v1 = bounds[s], bounds[s + 1]
+        tmax_s.append(_lib.tile_max_buffer(E, C[v0:v1]))
         _lib.cce_forward_shard(E, C[v0:v1], targets, v0, ignore_index, lse=lse_s[s],
-                               target_logit=zt_s[s])
+                               target_logit=zt_s[s], tile_max=tmax_s[s])
     loss, lse = _lib.cce_merge_shards(lse_s, zt_s, targets, V, ignore_index, err_flag=err_flag)
     if dloss is None:
         dloss = torch.ones(N, dtype=torch.float32, device=dev)
@@ -54,6 +56,7 @@ def forward_backward(E, C, targets, bounds, ignore_index: int = -100, filter_eps
     for s in range(S):
         v0, v1 = bounds[s], bounds[s + 1]
         dE_s, _ = _lib.cce_backward_shard(dloss, E, C[v0:v1], targets, lse, v0, ignore_index,
-                                          filter_eps, dC=dC[v0:v1], grad_dtype=gdt)
+                                          filter_eps, tile_max=tmax_s[s], dC=dC[v0:v1],
+                                          grad_dtype=gdt)
         dE += dE_s                      # the all-reduce over devices
     return loss, lse, dE.to(gdt), dC

@@ -65,7 +65,8 @@ def test_status_strings(lib):
 def test_workspace_has_no_tokens_times_vocabulary_term(lib, dt):
     """Extra device bytes are bounded by a per-token constant that does not grow with V:
     forward <= 8 bytes x 256 ranges per token, backward <= two chunks of 8192 vocabulary
-    columns of G per (padded) token plus their block flags, plus an fp32 dE accumulator."""
+    columns of G per (padded) token plus their block flags, plus an fp32 dE accumulator and
+    one float per 256-token tile."""
     sz = 4 if dt == 0 else 2
     for V, D in ((256000, 2304), (128256, 4096), (32000, 2048), (1000, 64), (10 ** 6, 64)):
         for N in (1, 255, 4096, 8192, 65536):
@@ -74,7 +75,8 @@ def test_workspace_has_no_tokens_times_vocabulary_term(lib, dt):
             bb = lib.cce_backward_workspace_bytes(N, V, D, dt)
             mb = lib.cce_loss_mean_workspace_bytes(N, V, D, dt)
             assert 0 < fb <= 2048 * N + 256
-            assert 0 < bb <= 2 * (pad * 8192 * sz + pad * 2 + 256) + N * D * 4 + 256
+            assert 0 < bb <= (2 * (pad * 8192 * sz + pad * 2 + 256) + N * D * 4 + 256
+                              + pad // 256 * 4 + 256)
             assert fb + bb < mb <= fb + bb + 8 * (N + 64) + 512
     # the logits of one config-sized problem would be 4 N V bytes; the workspace is far below
     N, V, D = 8192, 256000, 2304
@@ -117,11 +119,11 @@ def _fake(n=1):
 def test_forward_validation(lib):
     ok_ws = lib.cce_forward_workspace_bytes(16, 100, 64, 1)
     args = lambda **k: dict(dict(E=_fake(1), C=_fake(2), t=_fake(3), N=16, V=100, D=64, dt=1,
-                                 ii=-100, loss=_fake(4), lse=_fake(5), ws=_fake(6), wsb=ok_ws,
-                                 err=None, st=None), **k)
+                                 ii=-100, loss=_fake(4), lse=_fake(5), tm=None, ws=_fake(6),
+                                 wsb=ok_ws, err=None, st=None), **k)
     call = lambda a: lib.cce_forward(a["E"], a["C"], a["t"], a["N"], a["V"], a["D"], a["dt"],
-                                     a["ii"], a["loss"], a["lse"], a["ws"], a["wsb"], a["err"],
-                                     a["st"])
+                                     a["ii"], a["loss"], a["lse"], a["tm"], a["ws"], a["wsb"],
+                                     a["err"], a["st"])
     assert call(args(N=-1)) == 1
     assert call(args(V=0)) == 1
     assert call(args(D=60)) == 1
@@ -138,13 +140,21 @@ def test_forward_validation(lib):
     assert call(args(N=0, E=None, C=None, t=None, loss=None, lse=None, ws=None)) == 0
     for name in ("E", "C", "ws"):                      # 16-byte vectors: misaligned -> rejected
         assert call(args(**{name: ctypes.c_void_p(0x1008)})) == 1
+    assert call(args(tm=ctypes.c_void_p(0x1002))) == 1  # tile maxima: fp32, 4-byte aligned
+
+
+def test_tile_max_count(lib):
+    assert lib.cce_tile_max_count(8192, 256000, 2304, 1) == 32 * 1000 * 8
+    assert lib.cce_tile_max_count(1, 1, 8, 1) == 8
+    assert lib.cce_tile_max_count(0, 300, 8, 1) == 1 * 2 * 8
+    assert lib.cce_tile_max_count(16, 100, 60, 1) == 0              # invalid sizes
 
 
 def test_backward_validation(lib):
     ok_ws = lib.cce_backward_workspace_bytes(16, 100, 64, 1)
-    base = dict(dl=_fake(9), stride=1, E=_fake(1), C=_fake(2), t=_fake(3), lse=_fake(4), N=16,
-                V=100, D=64, dt=1, ii=-100, eps=0.0, dE=_fake(5), dC=_fake(6), gdt=0,
-                ws=_fake(7), wsb=ok_ws, sk=None, st=None)
+    base = dict(dl=_fake(9), stride=1, E=_fake(1), C=_fake(2), t=_fake(3), lse=_fake(4),
+                tm=None, N=16, V=100, D=64, dt=1, ii=-100, eps=0.0, dE=_fake(5), dC=_fake(6),
+                gdt=0, ws=_fake(7), wsb=ok_ws, sk=None, st=None)
     call = lambda **k: lib.cce_backward(*dict(base, **k).values())
     assert call(gdt=2) == 1
     assert call(eps=-1.0) == 1
@@ -157,6 +167,7 @@ def test_backward_validation(lib):
     assert call(D=4) == 1
     for name in ("E", "C", "dE", "dC", "ws"):
         assert call(**{name: ctypes.c_void_p(0x2004)}) == 1
+    assert call(tm=ctypes.c_void_p(0x2002)) == 1
     assert call(N=0, dC=ctypes.c_void_p(0x2004)) == 1
 
 

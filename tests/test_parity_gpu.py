@@ -405,3 +405,97 @@ def test_largest_vocabulary():
     d = S.small_case(64, 8, 1 << 24, "bf16", 44, 3.0, 1.1, 0.1)
     g = check_against_oracle(d, "bf16", S.dloss_weights(44, 64), 0.0, "v2^24")
     assert g["total"] == 1 * (1 << 18) and g["skipped"] == 0
+
+
+def _tile_max_oracle(E, C):
+    """The largest logit x log2(e) of each 128-row x 64-token part (wave w: rows 128 (w >> 2),
+    tokens 64 (w & 3)) of every 256 x 256 tile, from the oracle's logits; -inf when empty."""
+    N, V = E.shape[0], C.shape[0]
+    z = oracle.logits(E, C) / math.log(2.0)
+    n_tb, n_vt = -(-N // 256), -(-V // 256)
+    out = np.full((n_tb, n_vt, 8), -np.inf)
+    for tb in range(n_tb):
+        for vt in range(n_vt):
+            for w in range(8):
+                c0, r0 = 256 * tb + 64 * (w & 3), 256 * vt + 128 * (w >> 2)
+                blk = z[c0:min(N, c0 + 64), r0:min(V, r0 + 128)]
+                if blk.size:
+                    out[tb, vt, w] = blk.max()
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tile_maxima_match_the_logits(dtype):
+    """cce_forward's tile maxima against the oracle's logits (ragged N and V)."""
+    d = S.small_case(300, 136, 1100, dtype, 51, 3.0, 1.1, 0.1)
+    E, C, t = upload(d, dtype)
+    tm = cce.tile_max_buffer(E, C)
+    assert tm.numel() == 2 * 5 * 8
+    loss, lse = cce.cce_forward(E, C, t, II, tile_max=tm)
+    loss0, lse0 = cce.cce_forward(E, C, t, II)
+    assert torch.equal(lse, lse0) and torch.equal(loss, loss0)   # the output changes nothing else
+    ref = _tile_max_oracle(d["E"], d["C"])
+    g = tm.cpu().numpy()
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(g), fin)
+    np.testing.assert_allclose(g[fin], ref[fin], rtol=1e-5, atol=1e-4)
+
+
+def _far_tiles_case(dtype, seed):
+    """N = 600 tokens, V = 1280 rows; vocabulary tiles 1 and 3 (rows 256..511, 768..1023) get
+    logits near -200 for every token, so their G tiles can be skipped, except the one (tile 3,
+    token tile 0) that holds token 5's target."""
+    N, V, D = 600, 1280, 64
+    g = np.random.default_rng(seed)
+    E = np.concatenate([np.full((N, 1), 10.0), 0.1 * g.standard_normal((N, D - 1))],
+                       axis=1).astype(np.float32)
+    C = (0.05 * g.standard_normal((V, D))).astype(np.float32)
+    far = np.r_[256:512, 768:1024]
+    C[far, 0] = -20.0
+    if dtype == "bf16":
+        E, C = S.bf16_round(E), S.bf16_round(C)
+    t = g.choice(np.setdiff1d(np.arange(V), far), size=N).astype(np.int64)
+    t[5] = 800
+    t[7] = II
+    return {"E": E, "C": C, "targets": t}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tiles_proved_negligible_skip_their_recompute(dtype):
+    """With the forward's tile maxima, the backward skips the recompute of the far tiles (the
+    bound holds on 5 of them, checked here from the returned maxima) and returns bitwise the
+    same gradients and skip counts as without them, which match the oracle."""
+    d = _far_tiles_case(dtype, 61)
+    N, V = d["E"].shape[0], d["C"].shape[0]
+    w = S.dloss_weights(61, N)
+    E, C, t = upload(d, dtype)
+    tm = cce.tile_max_buffer(E, C)
+    loss, lse = cce.cce_forward(E, C, t, II, tile_max=tm)
+    dl = torch.from_numpy(w).to(DEV)
+    # the bound, from the returned maxima: max z log2 e - min lse log2 e over valid tokens
+    tmv = tm.cpu().numpy().reshape(3, 5, 8).max(axis=2)
+    l2 = lse.cpu().numpy() / math.log(2.0)
+    tt = d["targets"]
+    provable = 0
+    for tb in range(3):
+        rows = np.arange(256 * tb, min(N, 256 * tb + 256))
+        ok = tt[rows] != II
+        for vt in range(5):
+            has_t = np.any((tt[rows][ok] >= 256 * vt) & (tt[rows][ok] < 256 * vt + 256))
+            if not has_t and tmv[tb, vt] - l2[rows][ok].min() < math.log2(EPS) - 2.0 ** -10:
+                provable += 1
+    assert provable == 5, provable
+    out = {}
+    for name, arg in (("with", tm), ("without", None)):
+        stats = torch.zeros(2, dtype=torch.int64, device=DEV)
+        dE, dC = cce.cce_backward(dl, E, C, t, lse, II, EPS, tile_max=arg, skip_stats=stats)
+        torch.cuda.synchronize()
+        out[name] = (dE.cpu().numpy(), dC.cpu().numpy(), stats.tolist())
+    assert np.array_equal(out["with"][0], out["without"][0])
+    assert np.array_equal(out["with"][1], out["without"][1])
+    assert out["with"][2] == out["without"][2]
+    dE0, dC0, (sk, tot) = oracle.backward(d["E"], d["C"], d["targets"], w, II, filter_eps=EPS)
+    assert out["with"][2] == [sk, tot]
+    assert rel(out["with"][0], dE0) <= GRAD_TOL and rel(out["with"][1], dC0) <= GRAD_TOL
+    log(f"[far tiles {dtype}] provable {provable}, skipped {sk}/{tot}, "
+        f"dE {rel(out['with'][0], dE0):.2e} dC {rel(out['with'][1], dC0):.2e}")
