@@ -12,6 +12,8 @@ and drops single non-target entries below filter_eps * 2^-8 (sentence 9; 0 disab
 Every step of the computation runs in libcce's kernels (cce_forward / cce_backward /
 cce_loss_mean, which return the gradients in the dtype of E and C, accumulated in fp32); this
 module only routes tensors and gradients:
+  * "none" and "sum" keep the forward's tile maxima (when filtering) for the backward, which
+    then skips the recompute of tiles they prove negligible;
   * "none": per-token losses; the backward passes the upstream gradient as libcce's dloss;
   * "sum":  the per-token losses summed (dloss = the upstream scalar for every token);
   * "mean": libcce's mean call, which returns the mean over non-ignored tokens together with
@@ -30,20 +32,21 @@ FILTER_EPS = 2.0 ** -12
 class _PerToken(torch.autograd.Function):
     @staticmethod
     def forward(ctx, E, C, targets, ignore_index, filter_eps):
-        loss, lse = _lib.cce_forward(E, C, targets, ignore_index)
-        ctx.save_for_backward(E, C, targets, lse)
+        tmax = _lib.tile_max_buffer(E, C) if filter_eps > 0 else None
+        loss, lse = _lib.cce_forward(E, C, targets, ignore_index, tile_max=tmax)
+        ctx.save_for_backward(E, C, targets, lse, tmax)
         ctx.ignore_index = ignore_index
         ctx.filter_eps = filter_eps
         return loss
 
     @staticmethod
     def backward(ctx, grad_loss):
-        E, C, targets, lse = ctx.saved_tensors
+        E, C, targets, lse, tmax = ctx.saved_tensors
         if not (ctx.needs_input_grad[0] or ctx.needs_input_grad[1]):
             return None, None, None, None, None
         dloss = grad_loss.to(torch.float32).contiguous()
         dE, dC = _lib.cce_backward(dloss, E, C, targets, lse, ctx.ignore_index, ctx.filter_eps,
-                                   grad_dtype=E.dtype)
+                                   tile_max=tmax, grad_dtype=E.dtype)
         return (dE if ctx.needs_input_grad[0] else None,
                 dC if ctx.needs_input_grad[1] else None, None, None, None)
 
@@ -51,20 +54,21 @@ class _PerToken(torch.autograd.Function):
 class _Sum(torch.autograd.Function):
     @staticmethod
     def forward(ctx, E, C, targets, ignore_index, filter_eps):
-        loss, lse = _lib.cce_forward(E, C, targets, ignore_index)
-        ctx.save_for_backward(E, C, targets, lse)
+        tmax = _lib.tile_max_buffer(E, C) if filter_eps > 0 else None
+        loss, lse = _lib.cce_forward(E, C, targets, ignore_index, tile_max=tmax)
+        ctx.save_for_backward(E, C, targets, lse, tmax)
         ctx.ignore_index = ignore_index
         ctx.filter_eps = filter_eps
         return loss.sum()
 
     @staticmethod
     def backward(ctx, grad_sum):
-        E, C, targets, lse = ctx.saved_tensors
+        E, C, targets, lse, tmax = ctx.saved_tensors
         if not (ctx.needs_input_grad[0] or ctx.needs_input_grad[1]):
             return None, None, None, None, None
         dloss = grad_sum.to(torch.float32).reshape(1).contiguous()   # one scalar for all tokens
         dE, dC = _lib.cce_backward(dloss, E, C, targets, lse, ctx.ignore_index, ctx.filter_eps,
-                                   grad_dtype=E.dtype)
+                                   tile_max=tmax, grad_dtype=E.dtype)
         return (dE if ctx.needs_input_grad[0] else None,
                 dC if ctx.needs_input_grad[1] else None, None, None, None)
 
