@@ -1,4 +1,4 @@
-"""ctypes binding of libcce (include/cce.h): argument marshalling only.
+"""ctypes binding of libcce (include/cce.h, include/cce_timing.h): argument marshalling only.
 
 Every step of the computation runs in the HIP kernels of libcce.so; this module only turns torch
 tensors into device pointers, sizes and the current HIP stream, allocates outputs and
@@ -27,25 +27,27 @@ _c_ptr, _i64, _sz, _i32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
 SIGNATURES = {
     "cce_status_string": (ctypes.c_char_p, [_i32]),
     "cce_forward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
-    "cce_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
-    "cce_loss_mean_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "cce_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
+    "cce_loss_mean_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "cce_forward_splits": (_i64, [_i64, _i64, _i64, _i32]),
     "cce_backward_chunk": (_i64, [_i64, _i64, _i64, _i32]),
+    "cce_backward_token_block": (_i64, [_i64, _i64, _i64, _i32]),
     "cce_tile_max_count": (_i64, [_i64, _i64, _i64, _i32]),
     "cce_forward": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _c_ptr, _c_ptr,
                            _c_ptr, _c_ptr, _sz, _c_ptr, _c_ptr]),
     "cce_backward": (_i32, [_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i64, _i64,
-                            _i64, _i32, _i64, _f32, _c_ptr, _c_ptr, _i32, _c_ptr, _sz, _c_ptr,
-                            _c_ptr]),
-    "cce_loss_mean": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _f32, _c_ptr,
-                             _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _sz, _c_ptr, _c_ptr, _c_ptr]),
+                            _i64, _i32, _i64, _f32, _f32, _c_ptr, _c_ptr, _i32, _c_ptr, _sz,
+                            _c_ptr, _c_ptr]),
+    "cce_loss_mean": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _f32, _f32,
+                             _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _sz, _c_ptr, _c_ptr,
+                             _c_ptr]),
     "cce_forward_shard": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _i64,
                                  _c_ptr, _c_ptr, _c_ptr, _c_ptr, _sz, _c_ptr]),
     "cce_merge_shards": (_i32, [_c_ptr, _c_ptr, _i64, _i64, _c_ptr, _i64, _i64, _c_ptr, _c_ptr,
                                 _c_ptr, _c_ptr]),
     "cce_backward_shard": (_i32, [_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i64,
-                                  _i64, _i64, _i32, _i64, _i64, _f32, _c_ptr, _c_ptr, _i32,
-                                  _c_ptr, _sz, _c_ptr, _c_ptr]),
+                                  _i64, _i64, _i32, _i64, _i64, _f32, _f32, _c_ptr, _c_ptr,
+                                  _i32, _c_ptr, _sz, _c_ptr, _c_ptr]),
     "cce_timing_begin": (_i32, [ctypes.c_uint32, ctypes.c_int32]),
     "cce_timing_end": (_i32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int64)]),
 }
@@ -125,12 +127,16 @@ def forward_workspace_bytes(N: int, V: int, D: int, dtype: torch.dtype) -> int:
     return int(lib().cce_forward_workspace_bytes(N, V, D, dtype_code(dtype)))
 
 
-def backward_workspace_bytes(N: int, V: int, D: int, dtype: torch.dtype) -> int:
-    return int(lib().cce_backward_workspace_bytes(N, V, D, dtype_code(dtype)))
+def backward_workspace_bytes(N: int, V: int, D: int, dtype: torch.dtype,
+                             grad_dtype: torch.dtype = torch.float32) -> int:
+    return int(lib().cce_backward_workspace_bytes(N, V, D, dtype_code(dtype),
+                                                  dtype_code(grad_dtype)))
 
 
-def loss_mean_workspace_bytes(N: int, V: int, D: int, dtype: torch.dtype) -> int:
-    return int(lib().cce_loss_mean_workspace_bytes(N, V, D, dtype_code(dtype)))
+def loss_mean_workspace_bytes(N: int, V: int, D: int, dtype: torch.dtype,
+                              grad_dtype: torch.dtype = torch.float32) -> int:
+    return int(lib().cce_loss_mean_workspace_bytes(N, V, D, dtype_code(dtype),
+                                                   dtype_code(grad_dtype)))
 
 
 def forward_splits(N: int, V: int, D: int, dtype: torch.dtype) -> int:
@@ -139,6 +145,10 @@ def forward_splits(N: int, V: int, D: int, dtype: torch.dtype) -> int:
 
 def backward_chunk(N: int, V: int, D: int, dtype: torch.dtype) -> int:
     return int(lib().cce_backward_chunk(N, V, D, dtype_code(dtype)))
+
+
+def backward_token_block(N: int, V: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().cce_backward_token_block(N, V, D, dtype_code(dtype)))
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
@@ -198,11 +208,12 @@ def _grad_outputs(N, V, D, dev, grad_dtype, dE, dC):
 
 
 def cce_backward(dloss, E, C, targets, lse, ignore_index: int = -100, filter_eps: float = 0.0,
-                 *, tile_max=None, dE=None, dC=None, grad_dtype=None, ws=None, skip_stats=None,
-                 stream=None):
+                 *, entry_floor: float = 0.0, tile_max=None, dE=None, dC=None, grad_dtype=None,
+                 ws=None, skip_stats=None, stream=None):
     """dE [N,D] and dC [V,D] in grad_dtype (torch.float32 by default, or torch.bfloat16).
     dloss: fp32 [N], or a 1-element tensor (scalar).  tile_max: the forward's tile maxima for
-    the same E, C and targets, or None."""
+    the same E, C and targets, or None.  entry_floor: 0 (off) or the softmax value below which
+    non-target entries of the kept blocks are dropped."""
     N, V, D, dt = _check_inputs(E, C, targets)
     dev = E.device
     if dloss.dtype != torch.float32 or not dloss.is_cuda:
@@ -213,19 +224,20 @@ def cce_backward(dloss, E, C, targets, lse, ignore_index: int = -100, filter_eps
     _check_vec("lse", lse, N, torch.float32, dev)
     _check_tile_max(tile_max, N, V, D, dt, dev)
     dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
-    need = lib().cce_backward_workspace_bytes(N, V, D, dt)
+    need = lib().cce_backward_workspace_bytes(N, V, D, dt, gcode)
     ws = workspace(need, dev) if ws is None else ws
     with torch.cuda.device(dev):
         _check("cce_backward", lib().cce_backward(
             _ptr(dloss), stride, _ptr(E), _ptr(C), _ptr(targets), _ptr(lse), _ptr(tile_max), N,
-            V, D, dt, ignore_index, float(filter_eps), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
-            ws.numel() * ws.element_size(), _ptr(skip_stats), _stream(stream)))
+            V, D, dt, ignore_index, float(filter_eps), float(entry_floor), _ptr(dE), _ptr(dC),
+            gcode, _ptr(ws), ws.numel() * ws.element_size(), _ptr(skip_stats),
+            _stream(stream)))
     return dE, dC
 
 
 def cce_loss_mean(E, C, targets, ignore_index: int = -100, filter_eps: float = 0.0, *,
-                  dE=None, dC=None, grad_dtype=None, ws=None, err_flag=None, skip_stats=None,
-                  stream=None):
+                  entry_floor: float = 0.0, dE=None, dC=None, grad_dtype=None, ws=None,
+                  err_flag=None, skip_stats=None, stream=None):
     """Mean loss over non-ignored tokens and its gradients (in grad_dtype, fp32 by default).
     Returns (mean[1], n_valid[1], dE, dC) as device tensors."""
     N, V, D, dt = _check_inputs(E, C, targets)
@@ -233,12 +245,12 @@ def cce_loss_mean(E, C, targets, ignore_index: int = -100, filter_eps: float = 0
     mean = torch.empty(1, dtype=torch.float32, device=dev)
     n_valid = torch.empty(1, dtype=torch.int64, device=dev)
     dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
-    need = lib().cce_loss_mean_workspace_bytes(N, V, D, dt)
+    need = lib().cce_loss_mean_workspace_bytes(N, V, D, dt, gcode)
     ws = workspace(need, dev) if ws is None else ws
     with torch.cuda.device(dev):
         _check("cce_loss_mean", lib().cce_loss_mean(
             _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, float(filter_eps),
-            _ptr(mean), _ptr(n_valid), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
+            float(entry_floor), _ptr(mean), _ptr(n_valid), _ptr(dE), _ptr(dC), gcode, _ptr(ws),
             ws.numel() * ws.element_size(), _ptr(err_flag), _ptr(skip_stats), _stream(stream)))
     return mean, n_valid, dE, dC
 
@@ -286,8 +298,9 @@ def cce_merge_shards(lse_shards, target_logits, targets, V_total: int, ignore_in
 
 
 def cce_backward_shard(dloss, E, C_shard, targets, lse, vocab_offset: int,
-                       ignore_index: int = -100, filter_eps: float = 0.0, *, tile_max=None,
-                       dE=None, dC=None, grad_dtype=None, ws=None, skip_stats=None, stream=None):
+                       ignore_index: int = -100, filter_eps: float = 0.0, *,
+                       entry_floor: float = 0.0, tile_max=None, dE=None, dC=None,
+                       grad_dtype=None, ws=None, skip_stats=None, stream=None):
     """One vocabulary shard's backward with the merged LSE: (this shard's term of dE, the
     shard's rows of dC)."""
     N, V, D, dt = _check_inputs(E, C_shard, targets)
@@ -300,13 +313,13 @@ def cce_backward_shard(dloss, E, C_shard, targets, lse, vocab_offset: int,
     _check_vec("lse", lse, N, torch.float32, dev)
     _check_tile_max(tile_max, N, V, D, dt, dev)
     dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
-    need = lib().cce_backward_workspace_bytes(N, V, D, dt)
+    need = lib().cce_backward_workspace_bytes(N, V, D, dt, gcode)
     ws = workspace(need, dev) if ws is None else ws
     with torch.cuda.device(dev):
         _check("cce_backward_shard", lib().cce_backward_shard(
             _ptr(dloss), stride, _ptr(E), _ptr(C_shard), _ptr(targets), _ptr(lse),
             _ptr(tile_max), N, V, D, dt, ignore_index, int(vocab_offset), float(filter_eps),
-            _ptr(dE), _ptr(dC), gcode, _ptr(ws), ws.numel() * ws.element_size(),
+            float(entry_floor), _ptr(dE), _ptr(dC), gcode, _ptr(ws), ws.numel() * ws.element_size(),
             _ptr(skip_stats), _stream(stream)))
     return dE, dC
 

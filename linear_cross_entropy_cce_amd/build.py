@@ -1,13 +1,13 @@
 """Builds libcce.so (the gfx950 HIP kernels and the C ABI of include/cce.h) in-tree with hipcc."""
 from __future__ import annotations
 
+import glob
 import os
 import shutil
 import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "cce_api.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcce.so")
 ARCH = "gfx950"
@@ -20,12 +20,19 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libcce)")
 
 
+def sources() -> list[str]:
+    """Every HIP translation unit of the library (csrc/*.hip)."""
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+
+
 def compile_command(out: str) -> list[str]:
+    # -packed-fp32-ops: the gfx950 code generator emits no packed fp32 VALU forms (scalar fp32
+    # math only).  The device pass honours it; hipcc's host pass, which compiles the same files
+    # for x86, prints that it does not know the feature, which is harmless.
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            # packed fp32 VALU forms are left to nothing: scalar fp32 math only
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wno-unused-command-line-argument",
-            "-I", INCLUDE, "-I", os.path.join(PKG, "csrc"), SRC, "-o", out]
+            "-I", INCLUDE, "-I", os.path.join(PKG, "csrc"), *sources(), "-o", out]
 
 
 def build(verbose: bool = False) -> str:

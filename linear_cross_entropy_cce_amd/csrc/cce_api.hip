@@ -1,11 +1,14 @@
-// libcce C ABI: argument validation, launch planning and kernel launches (include/cce.h).
+// libcce C ABI: argument validation, launch planning and kernel launches (include/cce.h,
+// include/cce_timing.h).
 //
 // Host-side plan for the Cut Cross-Entropy abstract's method (taxoreview.com page
 // dblp:393/3562, sentences 4-6 and 9):
 //   forward : k_fwd_lse over (token tile x vocabulary range), then k_fwd_finish;
-//   backward: k_bwd_g for the first vocabulary chunk of Vc rows, then one k_bwd_fused per
-//             chunk c (dE and dC of c, G of c + 1), all on the caller's stream; only the G of
-//             two chunks (N x Vc each) ever lives in the workspace.
+//   backward: the (token, vocabulary) plane is cut into pairs of a token block (<= Nc tokens)
+//             and a vocabulary chunk (<= Vc rows), taken chunk by chunk and, within a chunk,
+//             block by block.  k_bwd_g recomputes the first pair's G, then one k_bwd_fused per
+//             pair p computes dE and dC of p and the G of p + 1, all on the caller's stream;
+//             only the G of two pairs (Nc x Vc each) ever lives in the workspace.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -16,6 +19,7 @@
 #include <vector>
 
 #include "cce.h"
+#include "cce_timing.h"
 
 #ifndef CCE_KB
 #define CCE_KB 128
@@ -92,32 +96,66 @@ int64_t env_int(const char* name, int64_t dflt) {
   return (end && *end == 0 && x > 0) ? (int64_t)x : dflt;
 }
 
-// Vocabulary chunk width of the backward (multiple of 256).  CCE_VC overrides the default.
-int64_t plan_chunk(int64_t V) {
-  static const int64_t vc_env = env_int("CCE_VC", 8192);
-  int64_t vc = std::max<int64_t>(256, std::min<int64_t>(vc_env, 8192) / 256 * 256);
-  return std::min<int64_t>(vc, ceil_div(V, kTile) * kTile);
+// Balanced split of `tiles` 256-wide tiles into the fewest parts of at most `max_tiles` each:
+// part i covers tiles [i * tiles / parts, (i + 1) * tiles / parts), so parts differ by at most
+// one tile and none is a short tail.
+struct Split {
+  int64_t parts, tiles;
+  int64_t begin(int64_t i) const { return i * tiles / parts; }
+  int64_t widest() const { return ceil_div(tiles, parts); }
+};
+Split balanced(int64_t tiles, int64_t max_tiles) {
+  Split s;
+  s.tiles = tiles;
+  s.parts = ceil_div(tiles, std::max<int64_t>(max_tiles, 1));
+  return s;
 }
 
-// Backward workspace: G and flags of two chunks in flight (c and c + 1), then the fp32 dE
-// accumulator used when the gradients are requested in bf16, then the smallest lse log2(e) of
-// each token tile (for skipping tiles with the forward's tile maxima).
+// Vocabulary chunks of the backward: at most 8192 rows (32 tiles) each; CCE_VC (a multiple of
+// 256, at most 8192) narrows them.
+Split plan_chunks(int64_t V) {
+  static const int64_t vc_env = env_int("CCE_VC", 8192);
+  const int64_t vc = std::max<int64_t>(kTile, std::min<int64_t>(vc_env, 8192) / kTile * kTile);
+  return balanced(ceil_div(V, kTile), vc / kTile);
+}
+// Token blocks of the backward: at most 16384 tokens for bf16 inputs and 8192 for fp32 (so the
+// G store of two pairs stays within 512 MiB); CCE_NC (a multiple of 256) overrides it.
+Split plan_blocks(int64_t N, cce_dtype dt) {
+  static const int64_t nc_env = env_int("CCE_NC", 0);
+  const int64_t dflt = dt == CCE_BF16 ? 16384 : 8192;
+  const int64_t nc =
+      nc_env > 0 ? std::max<int64_t>(kTile, std::min<int64_t>(nc_env, 65536)) / kTile * kTile
+                 : dflt;
+  return balanced(ceil_div(std::max<int64_t>(N, 1), kTile), nc / kTile);
+}
+int64_t plan_chunk(int64_t V) { return plan_chunks(V).widest() * kTile; }
+
+// Backward workspace: G and flags of two pairs in flight (p and p + 1, Nc x Vc each), the
+// smallest lse log2(e) of each token tile (for skipping tiles with the forward's tile maxima),
+// and, for bf16 gradients only, the fp32 running sums: dE [N, D] over the chunks and one
+// chunk's dC [Vc, D] over the token blocks (when there is more than one block).
 struct BwdLayout {
-  int64_t n_pad, vc, fstride;
-  size_t g_bytes, flag_bytes, acc_offset, acc_bytes, tmin_offset, tmin_bytes, total;
+  Split blocks, chunks;
+  int64_t nc, vc, fstride, n_pad;
+  size_t g_bytes, flag_bytes, tmin_offset, de_offset, de_bytes, dc_offset, dc_bytes, total;
 };
-BwdLayout bwd_layout(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
+BwdLayout bwd_layout(int64_t N, int64_t V, int64_t D, cce_dtype dt, cce_dtype gdt) {
   BwdLayout L;
+  L.blocks = plan_blocks(N, dt);
+  L.chunks = plan_chunks(V);
+  L.nc = L.blocks.widest() * kTile;
+  L.vc = L.chunks.widest() * kTile;
   L.n_pad = ceil_div(std::max<int64_t>(N, 1), kTile) * kTile;
-  L.vc = plan_chunk(V);
   L.fstride = L.vc / 64;
-  L.g_bytes = align_up((size_t)L.n_pad * (size_t)L.vc * dtype_size(dt));
-  L.flag_bytes = align_up((size_t)(L.n_pad / 64) * (size_t)L.fstride);
-  L.acc_offset = 2 * (L.g_bytes + L.flag_bytes);
-  L.acc_bytes = align_up((size_t)std::max<int64_t>(N, 1) * (size_t)D * 4);
-  L.tmin_offset = L.acc_offset + L.acc_bytes;
-  L.tmin_bytes = align_up((size_t)(L.n_pad / kTile) * 4);
-  L.total = L.tmin_offset + L.tmin_bytes;
+  L.g_bytes = align_up((size_t)L.nc * (size_t)L.vc * dtype_size(dt));
+  L.flag_bytes = align_up((size_t)(L.nc / 64) * (size_t)L.fstride);
+  L.tmin_offset = 2 * (L.g_bytes + L.flag_bytes);
+  L.de_offset = L.tmin_offset + align_up((size_t)(L.n_pad / kTile) * 4);
+  const bool bf = gdt == CCE_BF16;
+  L.de_bytes = bf ? align_up((size_t)std::max<int64_t>(N, 1) * (size_t)D * 4) : 0;
+  L.dc_offset = L.de_offset + L.de_bytes;
+  L.dc_bytes = bf && L.blocks.parts > 1 ? align_up((size_t)L.vc * (size_t)D * 4) : 0;
+  L.total = L.dc_offset + L.dc_bytes;
   return L;
 }
 size_t fwd_bytes(int64_t N, int64_t V) {
@@ -131,7 +169,8 @@ cce_status launch_status() {
   return hipGetLastError() == hipSuccess ? CCE_OK : CCE_ERR_HIP;
 }
 
-// Benchmark timing hook: event pairs around launches of the selected kernel kinds.
+// Benchmark timing hook (cce_timing.h): event pairs around launches of the selected kernel
+// kinds.  Process-wide and off unless a benchmark starts it.
 struct Timing {
   bool on = false;
   uint32_t mask = 0;
@@ -203,14 +242,17 @@ cce_status forward_impl(const T* E, const T* C, const int64_t* tgt, int64_t N, i
 template <typename T>
 cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const T* C,
                          const int64_t* tgt, const float* lse, const float* tile_max, int64_t N,
-                         int64_t V, int64_t D,
-                         int64_t ii, int64_t voff, float eps, void* dE, void* dC, cce_dtype gdt,
-                         void* ws, int64_t* skip_stats, hipStream_t st, cce_dtype dt) {
-  const BwdLayout L = bwd_layout(N, V, D, dt);
+                         int64_t V, int64_t D, int64_t ii, int64_t voff, float eps,
+                         float p_floor, void* dE, void* dC, cce_dtype gdt, void* ws,
+                         int64_t* skip_stats, hipStream_t st, cce_dtype dt) {
+  const BwdLayout L = bwd_layout(N, V, D, dt, gdt);
+  const bool bf = gdt == CCE_BF16;
   // dE accumulates over the chunks in fp32: in place, or in the workspace for bf16 output
-  float* dE_acc = gdt == CCE_F32 ? (float*)dE : (float*)((char*)ws + L.acc_offset);
-  const int64_t n_tb = L.n_pad / kTile, n_dt = ceil_div(D, kTile);
-  const int64_t n_chunks = ceil_div(V, L.vc);
+  float* dE_acc = bf ? (float*)((char*)ws + L.de_offset) : (float*)dE;
+  float* dC_acc = (float*)((char*)ws + L.dc_offset);   // bf16 gradients, several blocks
+  const int64_t n_dt = ceil_div(D, kTile);
+  const int64_t n_blk = L.blocks.parts, n_pairs = L.chunks.parts * n_blk;
+  const int64_t n_vt_all = ceil_div(V, kTile);
   if (skip_stats) {
     TimedLaunch tl(CCE_KERNEL_AUX, st);
     hipLaunchKernelGGL(k_skip_init, dim3(1), dim3(64), 0, st, skip_stats,
@@ -221,33 +263,53 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
   const bool tile_skip = tile_max != nullptr && eps > 0.f;
   if (tile_skip) {
     TimedLaunch tl(CCE_KERNEL_AUX, st);
-    hipLaunchKernelGGL(k_tile_lse_min, dim3((unsigned)n_tb), dim3(256), 0, st, lse, tgt, (int)N,
-                       ii, tile_lse_min);
+    hipLaunchKernelGGL(k_tile_lse_min, dim3((unsigned)(L.n_pad / kTile)), dim3(256), 0, st, lse,
+                       tgt, (int)N, ii, tile_lse_min);
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   }
-  // chunk c uses G / flag buffer c % 2
-  auto args = [&](int64_t c) {
+  // pair p = (chunk c, token block b), p = c * n_blk + b; its G and flags use buffer p % 2
+  auto args = [&](int64_t p) {
+    const int64_t c = p / n_blk, b = p % n_blk;
+    const int64_t n0 = L.blocks.begin(b) * kTile;
+    const int64_t n1 = std::min<int64_t>(N, L.blocks.begin(b + 1) * kTile);
+    const int64_t v0 = L.chunks.begin(c) * kTile;
+    const int64_t v1 = std::min<int64_t>(V, L.chunks.begin(c + 1) * kTile);
+    const int buf = (int)(p & 1);
     BwdArgs<T> A;
-    const int buf = (int)(c & 1);
-    A.E = E; A.C = C; A.tgt = tgt; A.lse = lse; A.dloss = dloss; A.dstride = dstride;
-    A.N = (int)N; A.V = (int)V; A.D = (int)D; A.n_pad = (int)L.n_pad;
-    A.v0 = (int)(c * L.vc);
-    A.vc = (int)std::min<int64_t>(L.vc, V - c * L.vc);
-    A.n_tb = (int)n_tb; A.n_vtc = (int)ceil_div(A.vc, kTile); A.n_dt = (int)n_dt;
+    A.E = E + n0 * D; A.C = C; A.tgt = tgt + n0; A.lse = lse + n0;
+    A.dloss = dloss + n0 * dstride; A.dstride = dstride;
+    A.N = (int)(n1 - n0); A.V = (int)V; A.D = (int)D;
+    A.n_pad = (int)(ceil_div(n1 - n0, kTile) * kTile);
+    A.v0 = (int)v0;
+    A.vc = (int)(v1 - v0);
+    A.n_tb = A.n_pad / kTile; A.n_vtc = (int)ceil_div(A.vc, kTile); A.n_dt = (int)n_dt;
     A.G = (T*)((char*)ws + buf * L.g_bytes);
     A.ldg = L.vc;
     A.flags = (uint8_t*)ws + 2 * L.g_bytes + buf * L.flag_bytes;
     A.fstride = (int)L.fstride;
-    A.eps = eps; A.ignore_index = ii; A.voff = voff;
+    A.eps = eps; A.p_floor = p_floor; A.ignore_index = ii; A.voff = voff;
     A.skip_count = (unsigned long long*)skip_stats;
-    A.dE = dE_acc; A.dC = dC; A.dc_bf16 = gdt == CCE_BF16 ? 1 : 0;
+    A.dE = dE_acc + n0 * D;
     A.accumulate = c > 0 ? 1 : 0;
+    // dC of the chunk: fp32 gradients add up in dC itself; bf16 gradients of several blocks
+    // in the chunk accumulator, the last block rounding the sum into dC
+    const bool last_blk = b == n_blk - 1;
+    if (!bf) {
+      A.dc_in = b > 0 ? (const float*)dC + v0 * D : nullptr;
+      A.dc_out = (float*)dC + v0 * D;
+      A.dc_bf16 = 0;
+    } else {
+      A.dc_in = b > 0 ? dC_acc : nullptr;
+      A.dc_out = last_blk ? (void*)((__bf16*)dC + v0 * D) : (void*)dC_acc;
+      A.dc_bf16 = last_blk ? 1 : 0;
+    }
     // without maxima, both pointers lead to the token-tile minima (at least 256 bytes) and the
     // kernel reads their first floats only
-    A.tile_max = tile_skip ? tile_max : tile_lse_min;
-    A.tile_lse_min = tile_lse_min;
+    const int64_t tb0 = n0 / kTile;
+    A.tile_max = tile_skip ? tile_max + tb0 * n_vt_all * kWaves : tile_lse_min;
+    A.tile_lse_min = tile_skip ? tile_lse_min + tb0 : tile_lse_min;
     A.tile_skip = tile_skip ? 1 : 0;
-    A.n_vt_all = (int)ceil_div(V, kTile);
+    A.n_vt_all = (int)n_vt_all;
     A.skip_bound = eps > 0.f ? std::log2(eps) - 1.f / 1024.f : -INFINITY;
     return A;
   };
@@ -261,10 +323,10 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
       hipLaunchKernelGGL((k_bwd_g<T, kKB, kNST, false>), grid, dim3(kThreads), 0, st, A0);
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   }
-  for (int64_t c = 0; c < n_chunks; ++c) {
-    const BwdArgs<T> A = args(c);
-    const bool more = c + 1 < n_chunks;
-    const BwdArgs<T> Nx = more ? args(c + 1) : A;
+  for (int64_t p = 0; p < n_pairs; ++p) {
+    const BwdArgs<T> A = args(p);
+    const bool more = p + 1 < n_pairs;
+    const BwdArgs<T> Nx = more ? args(p + 1) : A;
     const int r_de = grid_for(bwd_items(A.n_tb, A.n_dt));
     const int r_dc = grid_for(bwd_items(A.n_vtc, A.n_dt));
     const int r_g = more ? grid_for(bwd_items(Nx.n_tb, Nx.n_vtc)) : 0;
@@ -278,7 +340,7 @@ cce_status backward_impl(const float* dloss, int64_t dstride, const T* E, const 
                          r_de, r_dc);
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   }
-  if (gdt == CCE_BF16) {
+  if (bf) {
     TimedLaunch tl(CCE_KERNEL_AUX, st);
     const int64_t n = N * D;
     hipLaunchKernelGGL(k_f32_to_bf16, dim3((unsigned)std::min<int64_t>(ceil_div(n, 1024), 4096)),
@@ -308,9 +370,12 @@ size_t cce_forward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dt
   return fwd_bytes(N, V);
 }
 
-size_t cce_backward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
-  if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
-  return bwd_layout(N, V, D, dt).total;
+bool grad_dtype_ok(cce_dtype g) { return g == CCE_F32 || g == CCE_BF16; }
+
+size_t cce_backward_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dt,
+                                    cce_dtype gdt) {
+  if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D) || !grad_dtype_ok(gdt)) return 0;
+  return bwd_layout(N, V, D, dt, gdt).total;
 }
 
 int64_t cce_tile_max_count(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
@@ -318,9 +383,10 @@ int64_t cce_tile_max_count(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
   return tile_max_count(N, V);
 }
 
-size_t cce_loss_mean_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
-  if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
-  return fwd_bytes(N, V) + bwd_layout(N, V, D, dt).total + mean_extra_bytes(N);
+size_t cce_loss_mean_workspace_bytes(int64_t N, int64_t V, int64_t D, cce_dtype dt,
+                                     cce_dtype gdt) {
+  if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D) || !grad_dtype_ok(gdt)) return 0;
+  return fwd_bytes(N, V) + bwd_layout(N, V, D, dt, gdt).total + mean_extra_bytes(N);
 }
 
 int64_t cce_forward_splits(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
@@ -331,6 +397,11 @@ int64_t cce_forward_splits(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
 int64_t cce_backward_chunk(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
   if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
   return plan_chunk(V);
+}
+
+int64_t cce_backward_token_block(int64_t N, int64_t V, int64_t D, cce_dtype dt) {
+  if (!sizes_ok(N, V, D, dt) || !sizes_supported(N, V, D)) return 0;
+  return plan_blocks(N, dt).widest() * kTile;
 }
 
 cce_status cce_forward(const void* E, const void* C, const int64_t* targets, int64_t N,
@@ -360,14 +431,15 @@ cce_status backward_entry(const float* dloss, int64_t dloss_stride, const void* 
                           const void* C, const int64_t* targets, const float* lse,
                           const float* tile_max, int64_t N, int64_t V, int64_t D, cce_dtype dt,
                           int64_t ignore_index,
-                          int64_t voff, float filter_eps, void* dE, void* dC,
+                          int64_t voff, float filter_eps, float entry_floor, void* dE, void* dC,
                           cce_dtype grad_dtype, void* ws, size_t ws_bytes, int64_t* skip_stats,
                           void* stream) {
   if (!sizes_ok(N, V, D, dt)) return CCE_ERR_INVALID_ARGUMENT;
   if (!sizes_supported(N, V, D)) return CCE_ERR_UNSUPPORTED;
   if (!std::isfinite(filter_eps) || filter_eps < 0.f) return CCE_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(entry_floor) || entry_floor < 0.f) return CCE_ERR_INVALID_ARGUMENT;
   if (dloss_stride != 0 && dloss_stride != 1) return CCE_ERR_INVALID_ARGUMENT;
-  if (grad_dtype != CCE_F32 && grad_dtype != CCE_BF16) return CCE_ERR_INVALID_ARGUMENT;
+  if (!grad_dtype_ok(grad_dtype)) return CCE_ERR_INVALID_ARGUMENT;
   if (voff < 0) return CCE_ERR_INVALID_ARGUMENT;
   if (N == 0) {
     // nothing to reduce: dC is still defined (all zero) and so are the statistics
@@ -386,15 +458,16 @@ cce_status backward_entry(const float* dloss, int64_t dloss_stride, const void* 
   if (!dloss || !E || !C || !targets || !lse || !dE || !dC || !ws)
     return CCE_ERR_INVALID_ARGUMENT;
   if (!all_aligned16({E, C, dE, dC, ws}) || !aligned4(tile_max)) return CCE_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < bwd_layout(N, V, D, dt).total) return CCE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < bwd_layout(N, V, D, dt, grad_dtype).total) return CCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   if (dt == CCE_BF16)
     return backward_impl<__bf16>(dloss, dloss_stride, (const __bf16*)E, (const __bf16*)C,
                                  targets, lse, tile_max, N, V, D, ignore_index, voff,
-                                 filter_eps, dE, dC, grad_dtype, ws, skip_stats, st, dt);
+                                 filter_eps, entry_floor, dE, dC, grad_dtype, ws, skip_stats, st,
+                                 dt);
   return backward_impl<float>(dloss, dloss_stride, (const float*)E, (const float*)C, targets,
-                              lse, tile_max, N, V, D, ignore_index, voff, filter_eps, dE, dC,
-                              grad_dtype, ws, skip_stats, st, dt);
+                              lse, tile_max, N, V, D, ignore_index, voff, filter_eps,
+                              entry_floor, dE, dC, grad_dtype, ws, skip_stats, st, dt);
 }
 
 }  // namespace
@@ -404,22 +477,24 @@ extern "C" {
 cce_status cce_backward(const float* dloss, int64_t dloss_stride, const void* E, const void* C,
                         const int64_t* targets, const float* lse, const float* tile_max,
                         int64_t N, int64_t V, int64_t D, cce_dtype dt, int64_t ignore_index,
-                        float filter_eps, void* dE, void* dC, cce_dtype grad_dtype, void* ws,
-                        size_t ws_bytes, int64_t* skip_stats, void* stream) {
+                        float filter_eps, float entry_floor, void* dE, void* dC,
+                        cce_dtype grad_dtype, void* ws, size_t ws_bytes, int64_t* skip_stats,
+                        void* stream) {
   return backward_entry(dloss, dloss_stride, E, C, targets, lse, tile_max, N, V, D, dt,
-                        ignore_index, 0, filter_eps, dE, dC, grad_dtype, ws, ws_bytes,
-                        skip_stats, stream);
+                        ignore_index, 0, filter_eps, entry_floor, dE, dC, grad_dtype, ws,
+                        ws_bytes, skip_stats, stream);
 }
 
 cce_status cce_backward_shard(const float* dloss, int64_t dloss_stride, const void* E,
                               const void* C, const int64_t* targets, const float* lse,
                               const float* tile_max, int64_t N, int64_t V, int64_t D,
                               cce_dtype dt, int64_t ignore_index, int64_t vocab_offset,
-                              float filter_eps, void* dE, void* dC, cce_dtype grad_dtype,
-                              void* ws, size_t ws_bytes, int64_t* skip_stats, void* stream) {
+                              float filter_eps, float entry_floor, void* dE, void* dC,
+                              cce_dtype grad_dtype, void* ws, size_t ws_bytes,
+                              int64_t* skip_stats, void* stream) {
   return backward_entry(dloss, dloss_stride, E, C, targets, lse, tile_max, N, V, D, dt,
-                        ignore_index, vocab_offset, filter_eps, dE, dC, grad_dtype, ws, ws_bytes,
-                        skip_stats, stream);
+                        ignore_index, vocab_offset, filter_eps, entry_floor, dE, dC, grad_dtype,
+                        ws, ws_bytes, skip_stats, stream);
 }
 
 cce_status cce_forward_shard(const void* E, const void* C, const int64_t* targets, int64_t N,
@@ -462,20 +537,22 @@ cce_status cce_merge_shards(const float* lse_shards, const float* target_logits,
 
 cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, int64_t N,
                          int64_t V, int64_t D, cce_dtype dt, int64_t ignore_index,
-                         float filter_eps, float* loss_mean, int64_t* n_valid, void* dE,
-                         void* dC, cce_dtype grad_dtype, void* ws, size_t ws_bytes,
-                         int32_t* err_flag, int64_t* skip_stats, void* stream) {
+                         float filter_eps, float entry_floor, float* loss_mean,
+                         int64_t* n_valid, void* dE, void* dC, cce_dtype grad_dtype, void* ws,
+                         size_t ws_bytes, int32_t* err_flag, int64_t* skip_stats, void* stream) {
   if (!sizes_ok(N, V, D, dt)) return CCE_ERR_INVALID_ARGUMENT;
   if (!sizes_supported(N, V, D)) return CCE_ERR_UNSUPPORTED;
   if (!std::isfinite(filter_eps) || filter_eps < 0.f) return CCE_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(entry_floor) || entry_floor < 0.f) return CCE_ERR_INVALID_ARGUMENT;
+  if (!grad_dtype_ok(grad_dtype)) return CCE_ERR_INVALID_ARGUMENT;
   if (!loss_mean || !dC || !ws) return CCE_ERR_INVALID_ARGUMENT;
   if (N > 0 && (!E || !C || !targets || !dE)) return CCE_ERR_INVALID_ARGUMENT;
   if (!all_aligned16({dC, ws}) || (N > 0 && !all_aligned16({E, C, dE})))
     return CCE_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < cce_loss_mean_workspace_bytes(N, V, D, dt)) return CCE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < cce_loss_mean_workspace_bytes(N, V, D, dt, grad_dtype))
+    return CCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
-  if (grad_dtype != CCE_F32 && grad_dtype != CCE_BF16) return CCE_ERR_INVALID_ARGUMENT;
-  const size_t fb = fwd_bytes(N, V), bb = bwd_layout(N, V, D, dt).total;
+  const size_t fb = fwd_bytes(N, V), bb = bwd_layout(N, V, D, dt, grad_dtype).total;
   char* base = (char*)ws;
   char* extra = base + fb + bb;
   const size_t rows = (size_t)ceil_div(std::max<int64_t>(N, 1), 64) * 64;
@@ -487,7 +564,8 @@ cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, i
                        (const int64_t*)nullptr, 0, ignore_index, loss_mean, dloss, n_valid);
     if (launch_status() != CCE_OK) return CCE_ERR_HIP;
     return cce_backward(dloss, 0, E, C, targets, lse, nullptr, 0, V, D, dt, ignore_index,
-                        filter_eps, dE, dC, grad_dtype, base + fb, bb, skip_stats, stream);
+                        filter_eps, entry_floor, dE, dC, grad_dtype, base + fb, bb, skip_stats,
+                        stream);
   }
   cce_status s = cce_forward(E, C, targets, N, V, D, dt, ignore_index, loss, lse, nullptr, base,
                              fb, err_flag, stream);
@@ -499,7 +577,8 @@ cce_status cce_loss_mean(const void* E, const void* C, const int64_t* targets, i
   }
   if (launch_status() != CCE_OK) return CCE_ERR_HIP;
   return cce_backward(dloss, 0, E, C, targets, lse, nullptr, N, V, D, dt, ignore_index,
-                      filter_eps, dE, dC, grad_dtype, base + fb, bb, skip_stats, stream);
+                      filter_eps, entry_floor, dE, dC, grad_dtype, base + fb, bb, skip_stats,
+                      stream);
 }
 
 cce_status cce_timing_begin(uint32_t kind_mask, int32_t max_launches) {

@@ -1,10 +1,11 @@
 // Cut Cross-Entropy kernels for gfx950.
 //
-// Method: the Cut Cross-Entropy abstract (taxoreview.com page dblp:393/3562).  The loss needs
-// only the correct token's logit plus the log-sum-exp over all logits, computed on the fly
-// (sentences 4-5); matrix products and the log-sum-exp reduction run in on-chip memory so the
-// N x V logits never reach global memory (sentence 6); the backward skips gradient work whose
-// softmax contribution is negligible (sentence 9).
+// Method: the Cut Cross-Entropy abstract (taxoreview.com page dblp:393/3562, sentences 4-6
+// and 9).  Per token the loss is its LSE over the vocabulary less its target's logit, so the
+// forward keeps each logit tile in registers, folds it into a running (max, sum) and gathers
+// the one target logit separately; no N x V array is ever written.  The backward recomputes
+// the logit tiles and leaves out the blocks of the softmax gradient that the filter proves
+// negligible.
 //
 //   k_fwd_lse     S = C_tile E_tile^T on MFMA, online (max, sum exp) per token over the
 //                 workgroup's vocabulary range, one partial per (range, token).
@@ -13,9 +14,10 @@
 //   k_merge_shards  merge of per-shard LSEs and target logits into loss and LSE.
 //   k_bwd_g       recomputes S for a vocabulary chunk (tile_bwd_g), forms
 //                 G = dloss (softmax - onehot) in registers, flags negligible 64 x 64 blocks,
-//                 drops entries below the entry floor, stores the rest of G (bf16).
-//   k_bwd_fused   per chunk c: dE (+)= G_c C_c (tile_bwd_de) and dC_c = G_c^T E (tile_bwd_dc),
-//                 skipping flagged K stages, together with tile_bwd_g of chunk c + 1.
+//                 drops entries below the optional entry floor, stores the rest of G.
+//   k_bwd_fused   per (vocabulary chunk, token block) pair: dE (+)= G C_chunk (tile_bwd_de)
+//                 and dC_chunk (+)= G^T E_block (tile_bwd_dc), skipping flagged K stages,
+//                 together with tile_bwd_g of the next pair.
 //   k_f32_to_bf16, k_zero_f32, k_mean, k_skip_init  small helpers (bf16 gradient output,
 //                 empty batches, the mean-reduced call, the skip statistics).
 #pragma once
@@ -319,7 +321,9 @@ __global__ void k_merge_shards(const float* __restrict__ lse_s, const float* __r
 // and store G (chunk-local columns, row stride ldg) for the blocks that are kept.
 //   flags[(n / 64) * fstride + v_local / 64] = 1 if the block is skipped (G not stored).
 // ------------------------------------------------------------------------------------------
-// Arguments of the backward steps for one vocabulary chunk [v0, v0 + vc).
+// Arguments of the backward steps for one pair of a token block and a vocabulary chunk
+// [v0, v0 + vc).  The token-indexed pointers (E, tgt, lse, dloss, dE, tile_max, tile_lse_min)
+// start at the block's first token, so N and n_pad are the block's token counts.
 template <typename T>
 struct BwdArgs {
   const T* E;                 // [N, D]
@@ -336,13 +340,16 @@ struct BwdArgs {
   uint8_t* flags;             // [n_pad / 64, fstride] skipped 64 x 64 blocks of the chunk
   int fstride;
   float eps;
+  float p_floor;              // entry floor: non-target p below it are dropped (0: off)
   int64_t ignore_index;
   int64_t voff;               // vocabulary index of C's row 0 (a shard of a larger vocabulary)
   unsigned long long* skip_count;
-  float* dE;                  // [N, D] fp32 accumulator of dE over the chunks
-  void* dC;                   // [V, D] in the gradient dtype
-  int dc_bf16;                // dC written as bf16 (else fp32)
+  float* dE;                  // [N, D] fp32 running sum of dE over the chunks
   int accumulate;             // dE += (later chunks) instead of dE = (first chunk)
+  const float* dc_in;         // [vc, D] fp32 running sum of the chunk's dC over the token
+                              // blocks so far, or nullptr (first block: start from 0)
+  void* dc_out;               // [vc, D] where the chunk's dC (so far) goes
+  int dc_bf16;                // dc_out is bf16 (the last block of bf16 gradients), else fp32
   const float* tile_max;      // the forward's tile maxima (k_fwd_lse); readable when unused
   const float* tile_lse_min;  // [n_tb] smallest lse log2(e) of each token tile (k_tile_lse_min)
   int tile_skip;              // 1: skip tiles that tile_max proves negligible
@@ -470,13 +477,11 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
   run_stream<T, KB, NST, true, true>(0, n_k, n_k, issue, B, acc, wm, wn, lane);
 
   // epilogue: p = 2^(z log2 e - lse log2 e); G = coef (p - [row == target]); per lane and
-  // 64 x 64 block the largest p (independent maxima, no serial chains).  Entries with p below
-  // the entry floor eps * 2^-8 (eps scaled down by bf16's relative precision) are dropped from
-  // G, the target entry never: a subset of what dropping every non-target p < eps would drop
-  // (the CCE abstract, sentence 9).  The products over the zeros that result cost the MFMA
-  // units less power, which the board's power limit turns into clock.
+  // 64 x 64 block the largest p (independent maxima, no serial chains).  With the optional
+  // entry floor (the caller's p_floor > 0), non-target entries with p < p_floor are dropped
+  // from G; the target entry never is.  p_floor = 0 drops nothing (p < 0 never holds).
   const bool filter = eps > 0.f;
-  const float p_floor = eps * (1.f / 256.f);
+  const float p_floor = A.p_floor;
   const bool full = vl0 + kTile <= vc;
   if (!full) {
     // last tile of the chunk: rows at or past vc get p = 0
@@ -880,7 +885,7 @@ __device__ __forceinline__ void tile_bwd_de(const BwdArgs<T>& A, int lin, const 
 // Backward, step 3: dC[v0 + v, d] = sum over tokens of G[tok, v] E[tok, d] for the chunk.
 // A = G (MN-major, K = tokens), B = E (MN-major).
 // ------------------------------------------------------------------------------------------
-constexpr int kDcPiece = 4096;   // token stages handled per stage list of the dC product
+constexpr int kDcPiece = 1024;   // token stages handled per stage list of the dC product
 
 template <typename T, int KB, int NST>
 __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const Bufs<NST>& B,
@@ -894,7 +899,6 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
   const int D = A.D, N = A.N, n_pad = A.n_pad, vc = A.vc, n_vtc = A.n_vtc, n_dt = A.n_dt;
   const uint8_t* __restrict__ flags = A.flags;
   const int fstride = A.fstride;
-  const int64_t dc_off = (int64_t)A.v0 * A.D;
   int vt, dt;
   grouped_tile(lin, n_vtc, n_dt, vt, dt);
   if (vt >= n_vtc || dt >= n_dt) return;
@@ -907,14 +911,21 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
   uint32_t offA[I], offB[I];
   mn_offsets<T, KB>(offA, ldgb, vl0, (int)ldg, wave, lane);
   mn_offsets<T, KB>(offB, ldb, d0, D, wave, lane);
+  // dC of the chunk accumulates over the token blocks: the running sum (dc_in, fp32) is read
+  // into the accumulators up front, like dE's; the first block starts from zero
   Acc acc;
-  zero_acc(acc);
+  if (A.dc_in)
+    load_tile(A.dc_in, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc, lane);
+  else
+    zero_acc(acc);
+  bool live_any = false;
   for (int sbase = 0; sbase < n_stages; sbase += kPiece) {
     const int cnt = min(kPiece, n_stages - sbase);
     int seg[3];
     build_stage_list<KS, NST>(flags + (int64_t)((sbase * KS) >> 6) * fstride, fstride, cnt,
                               false, vt * 4, sList, sCnt, seg);
     const int n_act = seg[0] + seg[1] + seg[2];
+    live_any |= n_act > 0;
     int next_e = sList[0];   // list entry of the next issue() call (calls come in order)
     auto issue = [&](int i) {
       const bool live = i < n_act;   // past the end of the list: zeros
@@ -934,11 +945,12 @@ __device__ __forceinline__ void tile_bwd_dc(const BwdArgs<T>& A, int lin, const 
     run_segments<T, KB, NST, false, false>(seg, issue, B, acc, wm, wn, lane);
     __syncthreads();
   }
+  // nothing added and the running sum stays where it is: no store needed
+  if (!live_any && (const void*)A.dc_in == A.dc_out) return;
   if (A.dc_bf16)
-    store_tile_bf16((__bf16*)A.dC + dc_off, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc,
-                    lane);
+    store_tile_bf16((__bf16*)A.dc_out, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc, lane);
   else
-    store_tile((float*)A.dC + dc_off, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc, lane);
+    store_tile((float*)A.dc_out, D, vl0 + kWaveM * wm, vc, d0 + kWaveN * wn, D, acc, lane);
 }
 
 // Work items of the backward launches: one per tile (grouped_tile).

@@ -100,12 +100,16 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* p, int records) {
 // (it cannot tell the transposing reads apart from the buffer being filled).  The pipeline
 // waits for these loads itself (wait_stages before the barrier of the stage that reads them).
 // No register receives data, so no register can be reused while the load is in flight.
+// The LDS destination goes in through M0, named as an input operand ("{m0}"): the compiler
+// writes M0 itself before the statement and knows that the statement leaves it unchanged, so
+// M0 is never clobbered behind its back.  The s_nop is the wait state the hardware needs
+// between a write of M0 and an LDS-DMA load that reads it.
 __device__ __forceinline__ void lds_load16(Rsrc rs, char* lds, uint32_t voff, uint32_t soff) {
   const uint32_t la = (uint32_t)(uintptr_t)(lds_char_t*)lds;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "s"(__builtin_amdgcn_readfirstlane((int)la)), "v"(voff), "s"(rs), "s"(soff)
-               : "memory", "m0");
+               : "v"(voff), "s"(rs), "s"(soff), "{m0}"(__builtin_amdgcn_readfirstlane((int)la))
+               : "memory");
 }
 
 // Stage geometry.  KB = bytes of K per K-major operand row per stage (128 or 64): one

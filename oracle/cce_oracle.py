@@ -18,32 +18,32 @@ What is computed (all in float64, logits materialised one chunk at a time, never
   G[n, v]   = dloss[n] * (p[n, v] - [v == t[n]]) for valid n, 0 for ignored n
   dE        = G @ C,     dC = G^T @ E                         gradients of sum_n dloss[n] loss[n]
 
-Gradient filtering (s9: skip gradient work whose contribution is below numerical precision).
-The pages give neither a threshold nor a granularity.  Reading used here: the token x vocab
-plane is cut into aligned blocks of block_n x block_v (64 x 64 by default, the granularity the
-GPU library reports); a block is negligible iff every valid token row n in it has
-p[n, v] < filter_eps for every v in it AND no valid row's target lies in it.  Negligible
-blocks of G are set to zero before dE and dC are formed.  Inside the blocks that are kept, an
-entry whose p is below the entry floor filter_eps * 2^-8 (the threshold scaled down by bf16's
-relative precision) is set to zero too, unless it is the row's target entry: the dropped entries
-are a subset of those the element-wise reading of s9 (drop every non-target p < filter_eps)
-would drop.  filter_eps = 0 filters nothing.  Rows whose target is ignore_index have G = 0 and
-do not make a block significant.
+Gradient filtering (s9: leave out the parts of the gradient computation whose contribution is
+negligible).  The pages give neither a threshold nor a granularity.  Reading used here: the
+token x vocab plane is cut into aligned blocks of block_n x block_v (64 x 64 by default, the
+granularity the GPU library reports); a block is negligible iff every valid token row n in it
+has p[n, v] < filter_eps for every v in it AND no valid row's target lies in it.  Negligible
+blocks of G are set to zero before dE and dC are formed.  filter_eps = 0 filters nothing.
+Rows whose target is ignore_index have G = 0 and do not make a block significant.
+
+Optional entry floor (an approximation on top of the block filter, off unless entry_floor > 0):
+inside the blocks that are kept, a non-target entry whose p is below entry_floor is set to zero
+as well; the target entry never is.  Dropping a set S_n of entries of row n changes row n of dE
+by -dloss[n] sum_{v in S_n} p[n, v] C[v], so by at most dloss[n] * entry_floor * sum_v |C[v]|,
+and row v of dC by at most entry_floor * sum_n dloss[n] |E[n]|.
 
 Pins: every function here is checked in tests/test_oracle.py against mpmath brute force,
 closed forms, invariants, finite differences and torch's CPU cross-entropy; the block filter
-and the entry floor are checked against a pure-Python loop, constructed far-away blocks and a
-constructed target entry below the floor.
+is checked against a pure-Python loop and constructed far-away blocks; the entry floor against
+the closed form of equal classifier rows (every p = 1/V exactly, so a floor just above or just
+below 1/V drops every non-target entry or none) and the dropped-mass bounds above.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = ["logits", "forward", "backward", "loss_mean", "block_negligible", "entry_negligible",
-           "token_rows", "validate_targets", "ENTRY_FLOOR"]
-
-# Entry floor relative to filter_eps: 2^-8, the relative precision of bf16 (8 significant bits).
-ENTRY_FLOOR = 2.0 ** -8
+           "token_rows", "validate_targets"]
 
 
 def _f64(x):
@@ -131,18 +131,19 @@ def block_negligible(P, t_rows, valid_rows, filter_eps: float, n0: int, v0: int,
     return out
 
 
-def entry_negligible(P, t_rows, valid_rows, filter_eps: float, v0: int) -> np.ndarray:
-    """Entries of a probability sub-matrix P (columns v0..) below the entry floor
-    filter_eps * ENTRY_FLOOR, other than each valid row's target entry.  Returns bool, P's shape.
-    Rows that are not valid are never marked (their G is zero anyway)."""
-    out = (P < filter_eps * ENTRY_FLOOR) & valid_rows[:, None]
+def entry_negligible(P, t_rows, valid_rows, entry_floor: float, v0: int) -> np.ndarray:
+    """Entries of a probability sub-matrix P (columns v0..) below entry_floor, other than each
+    valid row's target entry.  Returns bool, P's shape.  Rows that are not valid are never
+    marked (their G is zero anyway); entry_floor = 0 marks nothing."""
+    out = (P < entry_floor) & valid_rows[:, None]
     rows = np.nonzero(valid_rows & (t_rows >= v0) & (t_rows < v0 + P.shape[1]))[0]
     out[rows, t_rows[rows] - v0] = False
     return out
 
 
 def backward(E, C, targets, dloss, ignore_index: int = -100, filter_eps: float = 0.0,
-             block_n: int = 64, block_v: int = 64, chunk: int = 256, vchunk: int = 65536):
+             block_n: int = 64, block_v: int = 64, chunk: int = 256, vchunk: int = 65536,
+             entry_floor: float = 0.0):
     """dE [N,D] and dC [V,D] in float64, plus (negligible blocks, total blocks).
 
     The LSE is recomputed here from E and C (the oracle never takes the GPU's LSE)."""
@@ -174,7 +175,7 @@ def backward(E, C, targets, dloss, ignore_index: int = -100, filter_eps: float =
             if neg.any():
                 for i, j in zip(*np.nonzero(neg)):
                     G[i * block_n:(i + 1) * block_n, j * block_v:(j + 1) * block_v] = 0.0
-            G[entry_negligible(P, tr, valid, filter_eps, v0)] = 0.0
+            G[entry_negligible(P, tr, valid, entry_floor, v0)] = 0.0
             dE[n0:n1] += G @ C64[v0:v1]
             dC[v0:v1] += G.T @ E_rows
     total = (-(-N // block_n)) * (-(-V // block_v))
@@ -182,7 +183,7 @@ def backward(E, C, targets, dloss, ignore_index: int = -100, filter_eps: float =
 
 
 def loss_mean(E, C, targets, ignore_index: int = -100, filter_eps: float = 0.0,
-              block_n: int = 64, block_v: int = 64):
+              block_n: int = 64, block_v: int = 64, entry_floor: float = 0.0):
     """Mean over valid tokens of the per-token loss, and its gradients.
 
     Reading: the mean divides by N_valid = number of tokens whose target is not
@@ -195,19 +196,27 @@ def loss_mean(E, C, targets, ignore_index: int = -100, filter_eps: float = 0.0,
         return 0.0, np.zeros((N, D)), np.zeros((C.shape[0], D)), 0
     mean = float(loss.sum() / n_valid)
     dE, dC, _ = backward(E, C, targets, np.full(N, 1.0 / n_valid), ignore_index, filter_eps,
-                         block_n, block_v)
+                         block_n, block_v, entry_floor=entry_floor)
     return mean, dE, dC, n_valid
 
 
 def token_rows(E, C, targets, rows, dloss_rows, ignore_index: int = -100,
-               filter_eps: float = 0.0, block_n: int = 64, block_v: int = 64,
-               vchunk: int = 16384):
+               filter_eps=0.0, block_n: int = 64, block_v: int = 64,
+               vchunk: int = 16384, entry_floor: float = 0.0, border_band: float = 1e-3):
     """The oracle restricted to a set of token rows, for checks at full size.
 
     rows must be a union of whole aligned token blocks (of block_n rows, the last one may be
     ragged) so that block filtering is decided exactly as on the full problem.  Returns loss,
     lse and dE for those rows, and dC_part = sum over those rows of G[n, :]^T E[n, :], which is
-    the whole of dC when every other row has dloss = 0."""
+    the whole of dC when every other row has dloss = 0.
+
+    filter_eps may be one threshold or a sequence of them: the gradients are then formed for
+    each threshold from the same softmax values and returned in result["by_eps"][eps] (the
+    top-level dE, dC_part and skipped are those of the first threshold).  For each threshold,
+    "border" lists the (token block, vocabulary block) pairs that hold no valid target and whose
+    largest softmax value lies within border_band of the threshold (relative): there a float32
+    evaluation of the same softmax may decide the block the other way."""
+    eps_list = tuple(float(e) for e in np.atleast_1d(filter_eps))
     rows = np.asarray(rows, dtype=np.int64)
     V = C.shape[0]
     D = E.shape[1]
@@ -215,31 +224,56 @@ def token_rows(E, C, targets, rows, dloss_rows, ignore_index: int = -100,
     valid = t != ignore_index
     d = _f64(dloss_rows).reshape(-1)
     E_rows = _f64(E[rows])
-    lse, zt = _rows_lse_and_target(E_rows, C, np.where(valid, t, -1), vchunk)
-    loss = np.where(valid, lse - zt, 0.0)
-    dE = np.zeros((len(rows), D))
-    dC_part = np.zeros((V, D))
-    # group rows by their aligned token block so the filter sees whole blocks
+    C64 = _f64(C)
+    loss = np.zeros(len(rows))
+    lse = np.zeros(len(rows))
+    per = {e: {"G": np.zeros((len(rows), V)), "skipped": 0, "border": []} for e in eps_list}
+    # one aligned token block at a time, so the filter sees whole blocks; the block's logits
+    # over the whole vocabulary are formed once (vocabulary chunk by chunk) and kept; the
+    # filtered G of all sampled rows is kept per threshold for the two products at the end
     blk = rows // block_n
-    skipped = 0
     for b in np.unique(blk):
         sel = np.nonzero(blk == b)[0]
-        for v0 in range(0, V, vchunk):
-            v1 = min(V, v0 + vchunk)
-            C_part = _f64(C[v0:v1])
-            z = E_rows[sel] @ C_part.T
-            P = np.exp(z - lse[sel, None])
-            G = P.copy()
-            ts = t[sel]
-            vs = valid[sel]
-            ridx = np.nonzero(vs & (ts >= v0) & (ts < v1))[0]
-            G[ridx, ts[ridx] - v0] -= 1.0
-            G *= (d[sel] * vs)[:, None]
-            neg = block_negligible(P, ts, vs, filter_eps, int(b) * block_n, v0, block_n, block_v)
-            skipped += int(neg.sum())
+        z = np.concatenate([logits(E_rows[sel], C64, v0, min(V, v0 + vchunk))
+                            for v0 in range(0, V, vchunk)], axis=1)
+        m = z.max(axis=1)
+        l = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+        ts = t[sel]
+        vs = valid[sel]
+        lse[sel] = l
+        ridx = np.nonzero(vs)[0]
+        loss[sel[ridx]] = l[ridx] - z[ridx, ts[ridx]]
+        P = np.exp(z - l[:, None])
+        del z
+        G0 = P.copy()
+        G0[ridx, ts[ridx]] -= 1.0
+        G0 *= (d[sel] * vs)[:, None]
+        G0[entry_negligible(P, ts, vs, entry_floor, 0)] = 0.0
+        # largest valid-row softmax value of each vocabulary block, and the blocks that hold a
+        # valid target (for the borderline list)
+        nvb = -(-V // block_v)
+        bmax = np.where(vs[:, None], P, 0.0)
+        bmax = np.array([bmax[:, j * block_v:(j + 1) * block_v].max() for j in range(nvb)])
+        has_t = np.zeros(nvb, dtype=bool)
+        has_t[ts[ridx] // block_v] = True
+        for e in eps_list:
+            r = per[e]
+            if e > 0:
+                near = np.nonzero(~has_t & (np.abs(bmax - e) <= border_band * e))[0]
+                r["border"] += [(int(b), int(j)) for j in near]
+            G = G0.copy()
+            neg = block_negligible(P, ts, vs, e, int(b) * block_n, 0, block_n, block_v)
+            r["skipped"] += int(neg.sum())
             for i, j in zip(*np.nonzero(neg)):
                 G[i * block_n:(i + 1) * block_n, j * block_v:(j + 1) * block_v] = 0.0
-            G[entry_negligible(P, ts, vs, filter_eps, v0)] = 0.0
-            dE[sel] += G @ C_part
-            dC_part[v0:v1] += G.T @ E_rows[sel]
-    return {"loss": loss, "lse": lse, "dE": dE, "dC_part": dC_part, "skipped": skipped}
+            r["G"][sel] = G
+            del G
+    for e in eps_list:
+        r = per[e]
+        G = r.pop("G")
+        r["dE"] = G @ C64
+        r["dC_part"] = G.T @ E_rows
+        del G
+    first = per[eps_list[0]]
+    return {"loss": loss, "lse": lse, "dE": first["dE"], "dC_part": first["dC_part"],
+            "skipped": first["skipped"], "by_eps": per}

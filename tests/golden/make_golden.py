@@ -20,10 +20,10 @@ def main():
     w = S.dloss_weights(77, 12)
     loss, lse = oracle.forward(d["E"], d["C"], d["targets"], S.IGNORE_INDEX)
     dE, dC, (sk, tot) = oracle.backward(d["E"], d["C"], d["targets"], w, S.IGNORE_INDEX,
-                                        filter_eps=0.01, block_n=2, block_v=4)
+                                        filter_eps=0.01, block_n=2, block_v=4, entry_floor=0.0)
     out = {"case": {"N": 12, "D": 16, "V": 40, "dtype": "bf16", "seed": 77, "c_scale": 8.0,
                     "zipf_s": 1.1, "ignore_frac": 0.25, "dloss_seed": 77, "filter_eps": 0.01,
-                    "block_n": 2, "block_v": 4},
+                    "entry_floor": 0.0, "block_n": 2, "block_v": 4},
            "targets": d["targets"].tolist(), "loss": loss.tolist(), "lse": lse.tolist(),
            "dE_rowsum": dE.sum(axis=1).tolist(), "dC_rowsum": dC.sum(axis=1).tolist(),
            "skipped": sk, "total": tot}

@@ -212,8 +212,8 @@ def test_out_of_range_target_is_an_error():
 
 
 # ---------------------------------------------------------------- gradient filtering
-def brute_filtered_grads(E, C, t, w, eps, bn, bv):
-    """Plain loops: per-element p, per-block decision, the entry floor (eps / 256, never the
+def brute_filtered_grads(E, C, t, w, eps, bn, bv, floor=0.0):
+    """Plain loops: per-element p, per-block decision, the optional entry floor (never the
     target entry), then the filtered G products."""
     N, V = E.shape[0], C.shape[0]
     z = [[float(np.dot(E[n], C[v])) for v in range(V)] for n in range(N)]
@@ -241,7 +241,7 @@ def brute_filtered_grads(E, C, t, w, eps, bn, bv):
                 G[i:i + bn, j:j + bv] = 0.0
     for n in range(N):
         for v in range(V):
-            if t[n] != II and v != t[n] and P[n, v] < eps / 256:
+            if t[n] != II and v != t[n] and P[n, v] < floor:
                 G[n, v] = 0.0
     return G @ C, G.T @ E, skipped
 
@@ -261,15 +261,17 @@ def test_block_filter_matches_brute_force(eps):
 
 
 def test_entry_floor_matches_brute_force():
-    """Entries below eps / 256 inside kept blocks are dropped, except a row's target entry; the
-    case puts row 0's target at its smallest logit, far below the floor."""
+    """With entry_floor = f, entries below f inside kept blocks are dropped, except a row's
+    target entry; the case puts row 0's target at its smallest logit, far below the floor."""
     E, C, t = rand_case(24, 16, 40, 5, scale=3.0, ignore=(9,))
     z0 = E[0] @ C.T
     t[0] = int(np.argmin(z0))
     w = np.random.default_rng(25).uniform(0.5, 1.5, 16)
     eps = 0.05
-    dE, dC, (sk, _) = oracle.backward(E, C, t, w, II, filter_eps=eps, block_n=4, block_v=8)
-    bE, bC, bsk = brute_filtered_grads(E, C, t, w, eps, 4, 8)
+    floor = eps / 256
+    dE, dC, (sk, _) = oracle.backward(E, C, t, w, II, filter_eps=eps, block_n=4, block_v=8,
+                                      entry_floor=floor)
+    bE, bC, bsk = brute_filtered_grads(E, C, t, w, eps, 4, 8, floor)
     assert sk == bsk
     np.testing.assert_allclose(dE, bE, rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(dC, bC, rtol=1e-10, atol=1e-12)
@@ -282,8 +284,67 @@ def test_entry_floor_matches_brute_force():
     kept = ~np.kron(neg, np.ones((4, 8), dtype=bool))[:16, :40] & (t != II)[:, None]
     assert (kept & (P < eps / 256)).sum() > 20 and (kept & (P >= eps / 256)).sum() > 20
     # without the floor the result differs by more than rounding
-    nE, _, _ = brute_filtered_grads(E, C, t, w, 0.0, 4, 8)
+    nE, _, _ = brute_filtered_grads(E, C, t, w, eps, 4, 8)
     assert np.linalg.norm(dE - nE) > 1e-9 * np.linalg.norm(nE)
+    # and the floor is off by default
+    d0 = oracle.backward(E, C, t, w, II, filter_eps=eps, block_n=4, block_v=8)
+    np.testing.assert_allclose(d0[0], nE, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-4])
+def test_entry_floor_closed_form_equal_rows(eps):
+    """Every classifier row equal to c: all logits of a token are equal, so every softmax entry
+    is exactly 1/V.  A floor just above 1/V drops every non-target entry: G keeps only
+    dloss_n (1/V - 1) at each target, so dE_n = dloss_n (1/V - 1) c and dC_v = (1/V - 1)
+    sum over tokens with target v of dloss_n E_n.  A floor just below 1/V drops nothing: dE = 0
+    (the row of G sums to 0) and dC_v = sum_n dloss_n (1/V - [t_n = v]) E_n.  The block filter
+    (eps below 1/V) keeps every block."""
+    rng = np.random.default_rng(31)
+    N, V, D = 40, 250, 6
+    E = rng.standard_normal((N, D))
+    c = rng.standard_normal(D)
+    C = np.tile(c, (V, 1))
+    t = rng.integers(0, V, N)
+    t[[3, 17]] = II
+    w = rng.uniform(0.5, 1.5, N)
+    valid = t != II
+    wv = np.where(valid, w, 0.0)
+    onehot = np.zeros((N, V))
+    onehot[np.nonzero(valid)[0], t[valid]] = 1.0
+    # floor above 1/V: only the target entries survive
+    dE, dC, (sk, _) = oracle.backward(E, C, t, w, II, filter_eps=eps, entry_floor=1.01 / V)
+    assert sk == 0
+    np.testing.assert_allclose(dE, (wv * (1.0 / V - 1.0))[:, None] * c[None, :], rtol=1e-12,
+                               atol=1e-12)
+    np.testing.assert_allclose(dC, (1.0 / V - 1.0) * (onehot * wv[:, None]).T @ E, rtol=1e-12,
+                               atol=1e-12)
+    # floor below 1/V: nothing is dropped
+    dE, dC, _ = oracle.backward(E, C, t, w, II, filter_eps=eps, entry_floor=0.99 / V)
+    np.testing.assert_allclose(dE, 0.0, atol=1e-12)
+    np.testing.assert_allclose(dC, ((1.0 / V) * valid[:, None] - onehot).T @ (wv[:, None] * E),
+                               rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("scale,seed", [(1.0, 41), (3.0, 42), (8.0, 43)])
+def test_entry_floor_dropped_mass_bounds(scale, seed):
+    """Dropping a set S_n of non-target entries of row n changes dE_n by
+    -dloss_n sum_{v in S_n} p[n, v] C_v and dC_v by -sum_{n: v in S_n} dloss_n p[n, v] E_n, with
+    every p in S_n below the floor f; so |ddE_n| <= dloss_n f sum_v |C_v| and
+    |ddC_v| <= f sum_n dloss_n |E_n| (triangle inequality).  Checked row by row for random
+    cases with the floor at 1/V and at 1/(4V) (f sum_v |C_v| stays below a typical |C_v|, so
+    dropping a target entry would break the bound)."""
+    E, C, t = rand_case(seed, 48, 60, 8, scale=scale, ignore=(5, 30))
+    w = np.random.default_rng(seed + 1).uniform(0.5, 1.5, 48)
+    wv = np.where(t != II, w, 0.0)
+    dE0, dC0, _ = oracle.backward(E, C, t, w, II)
+    for f in (1.0 / 60, 1.0 / 240):
+        dE, dC, _ = oracle.backward(E, C, t, w, II, entry_floor=f)
+        bE = wv * f * np.linalg.norm(C, axis=1).sum()
+        bC = f * (wv * np.linalg.norm(E, axis=1)).sum()
+        assert np.all(np.linalg.norm(dE - dE0, axis=1) <= bE * (1 + 1e-9) + 1e-15)
+        assert np.all(np.linalg.norm(dC - dC0, axis=1) <= bC * (1 + 1e-9) + 1e-15)
+        # the case drops something
+        assert np.linalg.norm(dE - dE0) > 1e-6 * np.linalg.norm(dE0)
 
 
 def test_filter_eps_zero_is_bitwise_unfiltered():
@@ -367,7 +428,7 @@ def test_oracle_reproduces_its_regression_fixture():
     loss, lse = oracle.forward(d["E"], d["C"], d["targets"], II)
     dE, dC, (sk, tot) = oracle.backward(d["E"], d["C"], d["targets"], w, II,
                                         filter_eps=c["filter_eps"], block_n=c["block_n"],
-                                        block_v=c["block_v"])
+                                        block_v=c["block_v"], entry_floor=c["entry_floor"])
     np.testing.assert_allclose(loss, g["loss"], rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse, g["lse"], rtol=0, atol=1e-12)
     np.testing.assert_allclose(dE.sum(1), g["dE_rowsum"], rtol=0, atol=1e-12)

@@ -2,7 +2,8 @@
 
 This shows the pins in test_oracle.py are sensitive to the plausible errors they are meant to
 catch: a missing max-subtraction, a sign error, a wrong index, a dropped term, an ignored
-target in the block filter, a forgotten ignore mask."""
+target in the block filter, a forgotten ignore mask, an entry floor that drops targets or
+compares the wrong quantity."""
 import numpy as np
 import pytest
 
@@ -68,14 +69,22 @@ def test_mutant_filter_counts_ignored_rows(monkeypatch):
 
 
 def test_mutant_entry_floor_drops_targets(monkeypatch):
-    def bad(P, t_rows, valid_rows, eps, v0):
-        return (P < eps * co.ENTRY_FLOOR) & valid_rows[:, None]
+    def bad(P, t_rows, valid_rows, floor, v0):
+        return (P < floor) & valid_rows[:, None]
     monkeypatch.setattr(co, "entry_negligible", bad)
     with pytest.raises(AssertionError):
-        T.test_entry_floor_matches_brute_force()
-
-
-def test_mutant_entry_floor_at_the_block_threshold(monkeypatch):
-    monkeypatch.setattr(co, "ENTRY_FLOOR", 1.0)
+        T.test_entry_floor_closed_form_equal_rows(0.0)
     with pytest.raises(AssertionError):
         T.test_entry_floor_matches_brute_force()
+
+
+def test_mutant_entry_floor_compares_the_gradient(monkeypatch):
+    """The floor applied to dloss * p rather than p (a plausible mix-up of the softmax value
+    with the gradient entry): the equal-rows closed form, whose dloss weights straddle 1, fails."""
+    orig = co.entry_negligible
+
+    def bad(P, t_rows, valid_rows, floor, v0):
+        return orig(P * 1.3, t_rows, valid_rows, floor, v0)
+    monkeypatch.setattr(co, "entry_negligible", bad)
+    with pytest.raises(AssertionError):
+        T.test_entry_floor_closed_form_equal_rows(0.0)

@@ -43,9 +43,10 @@ def test_small_cases(case, eps):
 
 
 def test_several_vocabulary_chunks():
-    """V = 20000 spans three backward chunks (8192 + 8192 + a ragged 3616)."""
+    """V = 20000 (79 vocabulary tiles) spans three balanced backward chunks of 26, 26 and 27
+    tiles (6656, 6656 and a ragged 6688 rows)."""
     d = S.small_case(300, 72, 20000, "bf16", 21, 3.0, 1.1, 0.05)
-    assert cce.backward_chunk(300, 20000, 72, torch.bfloat16) == 8192
+    assert cce.backward_chunk(300, 20000, 72, torch.bfloat16) == 27 * 256
     check_against_oracle(d, "bf16", S.dloss_weights(21, 300), EPS, "chunks")
 
 
@@ -250,10 +251,11 @@ def _wide_random_cases(n, seed=2025):
 @pytest.mark.parametrize("case", _random_cases(12) + _wide_random_cases(12), ids=lambda c: c[0])
 def test_random_shapes(case):
     """Seeded random shapes (ragged N, D and V, both dtypes, ignored rows, three thresholds)
-    against the oracle with the same threshold, element by element."""
+    against the oracle with the same threshold, element by element, and, when filtered,
+    against the unfiltered oracle."""
     name, N, D, V, dt, cs, z, ig, eps, seed = case
     d = S.small_case(N, D, V, dt, seed, cs, z, ig)
-    check_against_oracle(d, dt, S.dloss_weights(seed, N), eps, name, vs_unfiltered=False)
+    check_against_oracle(d, dt, S.dloss_weights(seed, N), eps, name)
 
 
 def _half_live_case(N, V, D, dtype, seed):
@@ -323,10 +325,11 @@ def test_vocabulary_relabelled_by_row_norm():
 
 
 @pytest.mark.parametrize("dtype,N", [("bf16", 270000), ("f32", 140000)])
-def test_dc_stage_lists_in_several_pieces(dtype, N):
-    """Token counts past one dC stage list (4096 stages of 64 bf16 or 32 fp32 tokens): the dC
-    product builds and runs its list piece by piece, here with stages live in one half, both or
-    neither, against the oracle with exactly its skipped blocks."""
+def test_many_token_blocks(dtype, N):
+    """Token counts far past one backward token block (270 000 bf16 tokens: 17 blocks of at
+    most 16384; 140 000 fp32 tokens: 18 blocks of at most 8192): each chunk's dC adds up over
+    the blocks, here with stages live in one half, both or neither, against the oracle with
+    exactly its skipped blocks."""
     V, D = 1000, 64
     d = _half_live_case(N, V, D, dtype, 73)
     w = S.dloss_weights(73, N)
@@ -337,8 +340,9 @@ def test_dc_stage_lists_in_several_pieces(dtype, N):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_last_vocabulary_chunk_narrower_than_a_block(dtype):
-    """V = 8192 + 40: the second backward chunk is 40 rows, less than one 64-row filter block
-    and one 256-row tile (its G tile, flags, dE stages and dC tile are all ragged)."""
+    """V = 8192 + 40 (33 vocabulary tiles, two balanced chunks of 16 and 17): the last tile of
+    the last chunk holds 40 rows, less than one 64-row filter block (its G tile, flags, dE
+    stages and dC tile are ragged), and many targets lie in it."""
     D = 72 if dtype == "bf16" else 68
     d = S.small_case(300, D, 8192 + 40, dtype, 29, 3.0, 1.1, 0.05)
     t = d["targets"].copy()
@@ -370,25 +374,79 @@ def test_ignore_index_inside_the_vocabulary():
     assert rel(g_dE, rE) <= GRAD_TOL and rel(dC.cpu().numpy(), rC) <= GRAD_TOL
 
 
-def test_entry_floor_matches_the_oracle_rule(monkeypatch):
-    """In fp32 (G kept in fp32) with eps = 0.1, the entries below the floor eps / 256 carry
-    enough of G (4e-3 of dE) that the GPU must match the oracle's rule closely and differ
-    clearly from the same oracle without the floor.  No block maximum lies within 1e-3 of eps,
-    so both sides skip the same 3 of 90 blocks."""
+def test_entry_floor_matches_the_oracle_rule():
+    """In fp32 (G kept in fp32) with eps = 0.1 and the optional entry floor at eps / 256, the
+    entries below the floor carry enough of G (4e-3 of dE) that the GPU must match the oracle's
+    rule closely and differ clearly from the same oracle without the floor.  No block maximum
+    lies within 1e-3 of eps, so both sides skip the same 3 of 90 blocks.  Without the argument
+    the floor is off."""
     d = S.small_case(300, 64, 1100, "f32", 41, 3.0, 1.1, 0.1)
     w = S.dloss_weights(41, 300)
-    eps = 0.1
-    g = gpu_run(d, "f32", w, eps)
+    eps, floor = 0.1, 0.1 / 256
+    g = gpu_run(d, "f32", w, eps, entry_floor=floor)
+    g0 = gpu_run(d, "f32", w, eps)
     E, C, t = d["E"], d["C"], d["targets"]
-    dE1, dC1, _ = oracle.backward(E, C, t, w, II, filter_eps=eps)
-    monkeypatch.setattr(oracle.cce_oracle, "ENTRY_FLOOR", 0.0)
+    dE1, dC1, _ = oracle.backward(E, C, t, w, II, filter_eps=eps, entry_floor=floor)
     dE0, dC0, _ = oracle.backward(E, C, t, w, II, filter_eps=eps)
     eE, eC = rel(g["dE"], dE1), rel(g["dC"], dC1)
     fE, fC = rel(dE1, dE0), rel(dC1, dC0)
     log(f"[entry floor] gpu vs oracle dE {eE:.2e} dC {eC:.2e}; floor effect dE {fE:.2e} dC {fC:.2e}")
-    assert g["skipped"] == 3
+    assert g["skipped"] == 3 and g0["skipped"] == 3
     assert eE < 1e-4 and eC < 1e-4
     assert fE > 20 * eE and fC > 20 * eC
+    assert rel(g0["dE"], dE0) < 1e-4 and rel(g0["dC"], dC0) < 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_entry_floor_closed_form_equal_rows(dtype):
+    """Every classifier row equal to c: every softmax entry is 1/V.  With the entry floor just
+    above 1/V only the target entries survive, so dE_n = dloss_n (1/V - 1) c and
+    dC_v = (1/V - 1) sum over tokens with target v of dloss_n E_n; with the floor just below
+    1/V nothing is dropped and dE = 0 (rows of G sum to zero; bf16 rounding of G leaves at most
+    2^-7 dloss_n |c|)."""
+    N, V, D = 300, 1000, 64
+    rng = np.random.default_rng(53)
+    E = S.bf16_round(rng.standard_normal((N, D)).astype(np.float32))
+    c = S.bf16_round(rng.standard_normal(D).astype(np.float32))
+    C = np.tile(c, (V, 1))
+    t = rng.integers(0, V, N)
+    t[::13] = II
+    w = S.dloss_weights(53, N)
+    valid = t != II
+    wv = np.where(valid, w, 0.0).astype(np.float64)
+    onehot = np.zeros((N, V))
+    onehot[np.nonzero(valid)[0], t[valid]] = 1.0
+    d = {"E": E, "C": C, "targets": t}
+    g = gpu_run(d, dtype, w, 0.0, entry_floor=1.01 / V)
+    ref_dE = (wv * (1.0 / V - 1.0))[:, None] * c[None, :].astype(np.float64)
+    ref_dC = (1.0 / V - 1.0) * (onehot * wv[:, None]).T @ E.astype(np.float64)
+    eE, eC = rel(g["dE"], ref_dE), rel(g["dC"], ref_dC)
+    g0 = gpu_run(d, dtype, w, 0.0, entry_floor=0.99 / V)
+    resid = np.linalg.norm(g0["dE"], axis=1) / (wv * np.linalg.norm(c) + 1e-30)
+    ref0_dC = ((1.0 / V) * valid[:, None] - onehot).T @ (wv[:, None] * E.astype(np.float64))
+    e0C = rel(g0["dC"], ref0_dC)
+    log(f"[entry floor closed form {dtype}] above 1/V: dE {eE:.2e} dC {eC:.2e}; below: "
+        f"max |dE_n| / (dloss_n |c|) {resid[valid].max():.2e}, dC {e0C:.2e}")
+    assert eE <= 1e-2 and eC <= 1e-2 and e0C <= 1e-2
+    assert resid[valid].max() <= 2.0 ** -7
+
+
+def test_bf16_gradients_over_several_token_blocks():
+    """bf16 gradients when the tokens span two backward token blocks (20 000 bf16 tokens: 79
+    tiles in blocks of 40 and 39) and the vocabulary two chunks: each chunk's dC adds up in
+    the fp32 chunk accumulator and the last block rounds it, so both gradients are exactly the
+    fp32 ones rounded to nearest even."""
+    N, V, D = 20000, 9000, 64
+    assert cce.backward_token_block(N, V, D, torch.bfloat16) == 40 * 256
+    d = S.small_case(N, D, V, "bf16", 57, 3.0, 1.1, 0.1)
+    E, C, t = upload(d, "bf16")
+    loss, lse = cce.cce_forward(E, C, t, II)
+    dl = torch.from_numpy(S.dloss_weights(57, N)).to(DEV)
+    e32, c32 = cce.cce_backward(dl, E, C, t, lse, II, EPS)
+    e16, c16 = cce.cce_backward(dl, E, C, t, lse, II, EPS, grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(e16, e32.to(torch.bfloat16)) and torch.equal(c16, c32.to(torch.bfloat16))
+    check_against_oracle(d, "bf16", S.dloss_weights(57, N), EPS, "two_token_blocks")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -441,50 +499,66 @@ def test_tile_maxima_match_the_logits(dtype):
     np.testing.assert_allclose(g[fin], ref[fin], rtol=1e-5, atol=1e-4)
 
 
-def _far_tiles_case(dtype, seed):
-    """N = 600 tokens, V = 1280 rows; vocabulary tiles 1 and 3 (rows 256..511, 768..1023) get
-    logits near -200 for every token, so their G tiles can be skipped, except the one (tile 3,
-    token tile 0) that holds token 5's target."""
-    N, V, D = 600, 1280, 64
+def _far_tiles_case(dtype, seed, V=1280, far_tiles=(1, 3)):
+    """N = 600 tokens; the given vocabulary tiles (256 rows each) get logits near -200 for
+    every token, so their G tiles can be skipped, except the one (the second far tile, token
+    tile 0) that holds token 5's target."""
+    N, D = 600, 64
     g = np.random.default_rng(seed)
     E = np.concatenate([np.full((N, 1), 10.0), 0.1 * g.standard_normal((N, D - 1))],
                        axis=1).astype(np.float32)
     C = (0.05 * g.standard_normal((V, D))).astype(np.float32)
-    far = np.r_[256:512, 768:1024]
+    far = np.concatenate([np.arange(256 * j, min(V, 256 * j + 256)) for j in far_tiles])
     C[far, 0] = -20.0
     if dtype == "bf16":
         E, C = S.bf16_round(E), S.bf16_round(C)
     t = g.choice(np.setdiff1d(np.arange(V), far), size=N).astype(np.int64)
-    t[5] = 800
+    t[5] = 256 * far_tiles[1] + 32
     t[7] = II
     return {"E": E, "C": C, "targets": t}
 
 
+FAR_LAYOUTS = {
+    # V, far vocabulary tiles: one backward chunk; or far tiles in all three chunks of
+    # V = 20000 (79 tiles: chunks of tiles 0-25, 26-51, 52-78), including a chunk's first tile
+    # and the ragged last tile
+    "one_chunk": (1280, (1, 3)),
+    "three_chunks": (20000, (5, 30, 26, 60, 78)),
+}
+
+
+@pytest.mark.parametrize("layout", sorted(FAR_LAYOUTS))
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_tiles_proved_negligible_skip_their_recompute(dtype):
+def test_tiles_proved_negligible_skip_their_recompute(dtype, layout):
     """With the forward's tile maxima, the backward skips the recompute of the far tiles (the
-    bound holds on 5 of them, checked here from the returned maxima) and returns bitwise the
-    same gradients and skip counts as without them, which match the oracle."""
-    d = _far_tiles_case(dtype, 61)
+    bound holds on all far tiles but the one holding a target, checked here from the returned
+    maxima; at V = 20000 the softmax is nearly uniform, about 1/V < eps, so tiles without a
+    target elsewhere qualify too), also in the G tiles computed inside the fused launches of
+    later chunks, and returns bitwise the same gradients and skip counts as without them, which
+    match the oracle."""
+    V0, far_tiles = FAR_LAYOUTS[layout]
+    d = _far_tiles_case(dtype, 61, V0, far_tiles)
     N, V = d["E"].shape[0], d["C"].shape[0]
+    n_vt = -(-V // 256)
     w = S.dloss_weights(61, N)
     E, C, t = upload(d, dtype)
     tm = cce.tile_max_buffer(E, C)
     loss, lse = cce.cce_forward(E, C, t, II, tile_max=tm)
     dl = torch.from_numpy(w).to(DEV)
     # the bound, from the returned maxima: max z log2 e - min lse log2 e over valid tokens
-    tmv = tm.cpu().numpy().reshape(3, 5, 8).max(axis=2)
+    tmv = tm.cpu().numpy().reshape(3, n_vt, 8).max(axis=2)
     l2 = lse.cpu().numpy() / math.log(2.0)
     tt = d["targets"]
-    provable = 0
+    provable = provable_far = 0
     for tb in range(3):
         rows = np.arange(256 * tb, min(N, 256 * tb + 256))
         ok = tt[rows] != II
-        for vt in range(5):
+        for vt in range(n_vt):
             has_t = np.any((tt[rows][ok] >= 256 * vt) & (tt[rows][ok] < 256 * vt + 256))
             if not has_t and tmv[tb, vt] - l2[rows][ok].min() < math.log2(EPS) - 2.0 ** -10:
                 provable += 1
-    assert provable == 5, provable
+                provable_far += vt in far_tiles
+    assert provable_far == 3 * len(far_tiles) - 1, provable_far
     out = {}
     for name, arg in (("with", tm), ("without", None)):
         stats = torch.zeros(2, dtype=torch.int64, device=DEV)
