@@ -100,6 +100,23 @@ cce_status cce_forward(const void* E, const void* C, const int64_t* targets,
                        float* loss, float* lse, float* tile_max, void* ws, size_t ws_bytes,
                        int32_t* err_flag, void* stream);
 
+/* cce_forward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments, results and errors
+ * as cce_forward without the workspace: the forward's scratch (the per-token LSE partials,
+ * cce_forward_workspace_bytes() of it) lives in a static device array of
+ * cce_forward_no_workspace_max_bytes() = 16 MiB that each GPU holds for the life of the
+ * process.  Problems needing more (N * splits * 8 bytes > 16 MiB, e.g. N > 2^21 with one
+ * vocabulary range) are refused on the host with CCE_ERR_WORKSPACE_TOO_SMALL.  The array's
+ * device address is looked up once per device, on the first call with that device current.
+ * Every call on one GPU shares the array: calls that overlap on one GPU (other streams, other
+ * host threads) race and must be ordered by the caller.  Nothing in it needs clearing; each
+ * call overwrites what it reads. */
+cce_status cce_forward_no_workspace(const void* E, const void* C, const int64_t* targets,
+                                    int64_t N, int64_t V, int64_t D, cce_dtype dtype,
+                                    int64_t ignore_index, float* loss, float* lse,
+                                    float* tile_max, int32_t* err_flag, void* stream);
+size_t cce_forward_no_workspace_max_bytes(void);
+
 /* Floats of cce_forward's tile_max for a problem: ceil(N/256) * ceil(V/256) * 8 (pure host;
  * 0 for invalid sizes). */
 int64_t cce_tile_max_count(int64_t N, int64_t V, int64_t D, cce_dtype dtype);

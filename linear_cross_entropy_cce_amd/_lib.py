@@ -41,6 +41,9 @@ SIGNATURES = {
     "cce_loss_mean": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _f32, _f32,
                              _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _sz, _c_ptr, _c_ptr,
                              _c_ptr]),
+    "cce_forward_no_workspace": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64,
+                                        _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+    "cce_forward_no_workspace_max_bytes": (_sz, []),
     "cce_forward_shard": (_i32, [_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i32, _i64, _i64,
                                  _c_ptr, _c_ptr, _c_ptr, _c_ptr, _sz, _c_ptr]),
     "cce_merge_shards": (_i32, [_c_ptr, _c_ptr, _i64, _i64, _c_ptr, _i64, _i64, _c_ptr, _c_ptr,
@@ -195,6 +198,29 @@ def cce_forward(E, C, targets, ignore_index: int = -100, *, loss=None, lse=None,
             _ptr(tile_max), _ptr(ws), ws.numel() * ws.element_size(), _ptr(err_flag),
             _stream(stream)))
     return loss, lse
+
+
+def cce_forward_no_workspace(E, C, targets, ignore_index: int = -100, *, loss=None, lse=None,
+                             tile_max=None, err_flag=None, stream=None):
+    """cce_forward for callers that cannot allocate: no workspace (the library's static 16 MiB
+    scratch of the current device instead), so no allocation happens when loss and lse are
+    passed in.  Calls that overlap on one GPU share that scratch and must be ordered."""
+    N, V, D, dt = _check_inputs(E, C, targets)
+    dev = E.device
+    loss = torch.empty(N, dtype=torch.float32, device=dev) if loss is None else loss
+    lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else lse
+    _check_vec("loss", loss, N, torch.float32, dev)
+    _check_vec("lse", lse, N, torch.float32, dev)
+    _check_tile_max(tile_max, N, V, D, dt, dev)
+    with torch.cuda.device(dev):
+        _check("cce_forward_no_workspace", lib().cce_forward_no_workspace(
+            _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, _ptr(loss), _ptr(lse),
+            _ptr(tile_max), _ptr(err_flag), _stream(stream)))
+    return loss, lse
+
+
+def forward_no_workspace_max_bytes() -> int:
+    return int(lib().cce_forward_no_workspace_max_bytes())
 
 
 def _grad_outputs(N, V, D, dev, grad_dtype, dE, dC):

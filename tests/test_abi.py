@@ -45,8 +45,10 @@ def test_binding_covers_the_header():
 
 def test_library_imports_no_allocation_copy_or_sync(lib):
     """The library never allocates, copies or clears device memory and never waits on the host:
-    its imports from the HIP runtime are kernel launches, the launch error query and the events
-    of the benchmark timing hook (whose end call waits for its own events)."""
+    its imports from the HIP runtime are kernel launches, the launch error query, the events of
+    the benchmark timing hook (whose end call waits for its own events), and, for the forward
+    that takes no workspace, the current device and the device address of its static scratch
+    array."""
     import shutil
     import subprocess
     import linear_cross_entropy_cce_amd as cce
@@ -58,7 +60,8 @@ def test_library_imports_no_allocation_copy_or_sync(lib):
            if line.split() and line.split()[-1].startswith("hip")}
     assert "hipLaunchKernel" in hip
     assert hip <= {"hipLaunchKernel", "hipGetLastError", "hipEventCreate", "hipEventDestroy",
-                   "hipEventRecord", "hipEventElapsedTime", "hipEventSynchronize"}, hip
+                   "hipEventRecord", "hipEventElapsedTime", "hipEventSynchronize",
+                   "hipGetDevice", "hipGetSymbolAddress"}, hip
 
 
 def test_status_strings(lib):
@@ -237,3 +240,22 @@ def test_binding_requires_gpu_tensors():
     E = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         cce.cce_forward(E, E, torch.zeros(4, dtype=torch.int64))
+
+
+def test_no_workspace_forward_refuses_on_the_host(lib):
+    """The forward without workspace refuses, before touching any pointer or the GPU, problems
+    whose scratch exceeds its 16 MiB (WORKSPACE_TOO_SMALL = 3), reports invalid sizes as
+    cce_forward does, and treats N = 0 as a no-op."""
+    assert lib.cce_forward_no_workspace_max_bytes() == 16 << 20
+    N = (1 << 21) + 256
+    assert lib.cce_forward_workspace_bytes(N, 256, 8, BF16) > 16 << 20
+    assert lib.cce_forward_workspace_bytes(1 << 21, 256, 8, BF16) == 16 << 20
+    f = lambda n, v, d, dt: lib.cce_forward_no_workspace(_fake(1), _fake(2), _fake(3), n, v, d,
+                                                         dt, -100, _fake(4), _fake(5), None,
+                                                         None, None)
+    assert f(N, 256, 8, BF16) == 3
+    assert f(16, 0, 8, BF16) == 1
+    assert f(16, 100, 12, BF16) == 1
+    assert f(16, 1 << 25, 8, BF16) == 2
+    assert lib.cce_forward_no_workspace(None, None, None, 0, 10, 8, BF16, -100, None, None,
+                                        None, None, None) == 0
