@@ -630,8 +630,9 @@ __device__ __forceinline__ void tile_bwd_g(const BwdArgs<T>& A, int lin, const B
         const int nl = 4 * i + (lane >> 4);
         const bf16x8_t v =
             *(const __attribute__((address_space(3))) bf16x8_t*)(stg + nl * 256 + ((c ^ (nl & 15)) << 4));
-        if (mine)
-          *(bf16x8_t*)(G + (int64_t)(nblk + nl) * ldg + vl0 + kWaveM * wm + 8 * c) = v;
+        if (mine)   // streamed out: the next launch reads it, this one never does
+          __builtin_nontemporal_store(
+              v, (bf16x8_t*)(G + (int64_t)(nblk + nl) * ldg + vl0 + kWaveM * wm + 8 * c));
       }
     }
   }
@@ -686,7 +687,9 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ in, int64_t 
 
 // Writes this wave's 128 x 64 accumulators to a row-major fp32 matrix out[rows][ld] at
 // (row0, col0); rows >= row_lim and columns >= col_lim are dropped.  For each register a
-// half-wave writes 32 consecutive columns (128 bytes).
+// half-wave writes 32 consecutive columns (128 bytes).  The stores are non-temporal: a tile's
+// result is read again by a later launch at the earliest, so it should not displace the
+// operand lines the running tiles share in the L2.
 __device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, int row0,
                                            int row_lim, int col0, int col_lim, const Acc& acc,
                                            int lane) {
@@ -697,8 +700,9 @@ __device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, 
       for (int ni = 0; ni < kNB; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          out[(int64_t)(row0 + 32 * mi + acc_row(r, lane)) * ld + col0 + 32 * ni + (lane & 31)] =
-              acc[mi][ni][r];
+          __builtin_nontemporal_store(
+              acc[mi][ni][r],
+              &out[(int64_t)(row0 + 32 * mi + acc_row(r, lane)) * ld + col0 + 32 * ni + (lane & 31)]);
   } else {
 #pragma unroll
     for (int mi = 0; mi < kMB; ++mi)
@@ -707,7 +711,8 @@ __device__ __forceinline__ void store_tile(float* __restrict__ out, int64_t ld, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = row0 + 32 * mi + acc_row(r, lane), col = col0 + 32 * ni + (lane & 31);
-          if (row < row_lim && col < col_lim) out[(int64_t)row * ld + col] = acc[mi][ni][r];
+          if (row < row_lim && col < col_lim)
+            __builtin_nontemporal_store(acc[mi][ni][r], &out[(int64_t)row * ld + col]);
         }
   }
 }
