@@ -8,9 +8,11 @@ targets, filter_eps=2^-12).  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-Flop accounting: 2 N V D for the forward and 6 N V D for the backward (logit recompute plus
-the dE and dC products), whatever the filter skips ("nominal"); the work actually executed
-with skipped blocks is reported beside it.
+Flop accounting.  The method's work (pct_bf16_peak, roofline): 2 N V D for the forward; for
+the backward 2 N V D for the logit recompute, less the 256 x 256 tiles that the forward's
+tile maxima prove negligible (never recomputed), plus 4 N V D for the dE and dC products,
+less the 64 x 64 blocks of G that the filter skips.  With nothing filtered this is the
+8 N V D of the dense computation, which is also reported, labelled as dense-equivalent.
 """
 from __future__ import annotations
 
@@ -33,6 +35,7 @@ SOURCES = ("linear_cross_entropy_cce_amd/csrc/cce_api.hip",
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources of the kernels and their launch plan (the profiles record it)."""
     h = hashlib.sha256()
     for p in SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
@@ -51,6 +54,30 @@ def traffic_from_profiles(kind: str, workload: str):
     if t.get("source_hash") != kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def tiles_proved_negligible(tmax, lse, t, N: int, V: int, eps: float) -> int:
+    """256 x 256 (token, vocabulary) tiles whose recompute the backward skips: the largest
+    logit of the tile (the forward's tile maxima, in log2 units) less the smallest LSE of the
+    tile's non-ignored tokens lies below log2(eps) by the kernel's margin of 2^-10, and no token
+    of the tile has its target among the tile's rows.  Counted on the GPU after the timed
+    region, for the flop accounting."""
+    import math
+    import torch
+    if eps <= 0:
+        return 0
+    n_tb, n_vt = -(-N // 256), -(-V // 256)
+    tm = tmax[:n_tb * n_vt * 8].view(n_tb, n_vt, 8).amax(dim=2)
+    l2 = lse * (1.0 / math.log(2.0))
+    valid = t != -100
+    pad = n_tb * 256 - N
+    l2v = torch.where(valid, l2, torch.full_like(l2, float("inf")))
+    lmin = torch.nn.functional.pad(l2v, (0, pad), value=float("inf")).view(n_tb, 256).amin(dim=1)
+    below = (tm - lmin[:, None]) < (math.log2(eps) - 2.0 ** -10)
+    has_t = torch.zeros(n_tb, n_vt, dtype=torch.bool, device=t.device)
+    tok = torch.arange(N, device=t.device)
+    has_t[tok[valid] // 256, t[valid] // 256] = True
+    return int((below & ~has_t).sum())
 
 
 def cpu_baseline(d, w, n_tokens: int) -> dict:
@@ -335,8 +362,12 @@ def main() -> int:
     ap.add_argument("--workload", default="gemma2_2b_head")
     ap.add_argument("--filter-eps", type=float, default=None,
                     help="override the workload's gradient filter threshold")
+    ap.add_argument("--entry-floor", type=float, default=0.0,
+                    help="optional entry floor of the backward (0: off, the block filter only)")
+    ap.add_argument("--no-tile-max", action="store_true",
+                    help="do not pass the forward's tile maxima to the backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=768)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--shards", type=int, default=0,
                     help="only time the vocabulary-sharded head emulated on one GPU with this "
                          "many shards against the unsharded step (one JSON line)")
@@ -400,17 +431,18 @@ def main() -> int:
     torch.cuda.synchronize()
     base_alloc = torch.cuda.memory_allocated()
     fws_b = cce.forward_workspace_bytes(N, V, D, tdt)
-    bws_b = cce.backward_workspace_bytes(N, V, D, tdt)
+    bws_b = cce.backward_workspace_bytes(N, V, D, tdt, torch.float32)
     fws = cce._lib.workspace(fws_b, dev)
     bws = cce._lib.workspace(bws_b, dev)
-    tmax = cce.tile_max_buffer(E, C)      # the forward's tile maxima, kept for the backward
-    tmax_b = tmax.numel() * 4
+    # the forward's tile maxima, kept for the backward (N x V / 2048 bytes)
+    tmax = None if args.no_tile_max else cce.tile_max_buffer(E, C)
+    tmax_b = 0 if tmax is None else tmax.numel() * 4
     torch.cuda.reset_peak_memory_stats()
 
     def step():
         cce.cce_forward(E, C, t, S.IGNORE_INDEX, loss=loss, lse=lse, tile_max=tmax, ws=fws)
-        cce.cce_backward(dloss, E, C, t, lse, S.IGNORE_INDEX, eps, tile_max=tmax, dE=dE, dC=dC,
-                         ws=bws, skip_stats=stats)
+        cce.cce_backward(dloss, E, C, t, lse, S.IGNORE_INDEX, eps, entry_floor=args.entry_floor,
+                         tile_max=tmax, dE=dE, dC=dC, ws=bws, skip_stats=stats)
 
     for _ in range(args.warmup):
         step()
@@ -430,21 +462,36 @@ def main() -> int:
     step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     clock = None if args.no_clock else sample_clock(step)
 
-    flop_fwd = 2.0 * N * V * D
-    flop_bwd = 6.0 * N * V * D
     skipped, total_blocks = (int(x) for x in stats.tolist())
     n_valid = int((d["targets"] != S.IGNORE_INDEX).sum())
     skip_frac = skipped / total_blocks if total_blocks else 0.0
-    tflops = (flop_fwd + flop_bwd) / (ms * 1e-3) / 1e12
+    n_tiles = -(-N // 256) * -(-V // 256)
+    tiles_skipped = 0 if tmax is None else tiles_proved_negligible(tmax, lse, t, N, V, eps)
+    tile_frac = tiles_skipped / n_tiles
+    flop_fwd = 2.0 * N * V * D
+    flop_recompute = 2.0 * N * V * D * (1.0 - tile_frac)
+    flop_products = 4.0 * N * V * D * (1.0 - skip_frac)
+    flop_method = flop_fwd + flop_recompute + flop_products
+    tflops = flop_method / (ms * 1e-3) / 1e12
+    tflops_dense = 8.0 * N * V * D / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
 
     # dominant kernel: the kind with the largest time per step
     per_step = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps}
                 for k, v in kernels.items()}
-    vc0 = min(cce.backward_chunk(N, V, D, tdt), V)      # width of the first chunk
+    # the first pair's recompute runs in bwd_g, the rest in the fused launches.  Blocks and
+    # chunks are balanced splits of 256-wide tiles (parts = ceil(tiles / widest part)), the
+    # first part floor(tiles / parts) tiles long.
+    def first_part(n, widest):
+        tiles = -(-n // 256)
+        parts = -(-tiles // (widest // 256))
+        return min(n, (tiles // parts) * 256)
+    nc0 = first_part(N, cce.backward_token_block(N, V, D, tdt))
+    vc0 = first_part(V, cce.backward_chunk(N, V, D, tdt))
+    first = (nc0 * vc0) / (N * V)
     flops_per_step = {"fwd_lse": flop_fwd,
-                      "bwd_g": 2.0 * N * vc0 * D,               # recompute of the first chunk
-                      "bwd_fused": 4.0 * N * V * D + 2.0 * N * (V - vc0) * D}
+                      "bwd_g": flop_recompute * first,
+                      "bwd_fused": flop_products + flop_recompute * (1.0 - first)}
     dom = max((k for k in per_step if k in flops_per_step), key=lambda k: per_step[k]["ms_per_step"])
     dom_ms_launch = kernels[dom][0] / kernels[dom][1]
     dom_flop_launch = flops_per_step[dom] / per_step[dom]["launches_per_step"]
@@ -471,12 +518,17 @@ def main() -> int:
         "data": "synthetic (seeded, cce_synth recipe; no model weights)",
         "config": {"workload": f"{w.name}: N={N} D={D} V={V} {w.dtype}, "
                                f"filter_eps={eps:g}", "N": N, "D": D, "V": V,
-                   "filter_eps": eps, "parallelism": "none (1 GPU)"},
-        "tflops_nominal": tflops,
+                   "filter_eps": eps, "entry_floor": args.entry_floor,
+                   "tile_max": tmax is not None, "parallelism": "none (1 GPU)"},
+        "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / peak,
-        "tflops_executed": (4.0 * N * V * D + 4.0 * N * V * D * (1.0 - skip_frac))
-                           / (ms * 1e-3) / 1e12,
+        "flops_counted": "method's work: forward 2NVD, recompute 2NVD less tiles proved "
+                         "negligible, dE and dC products 4NVD less skipped 64x64 blocks",
+        "tflops_dense_equivalent": tflops_dense,
+        "pct_bf16_peak_dense_equivalent": 100.0 * tflops_dense / peak,
         "skip_fraction_64x64_blocks": skip_frac,
+        "recompute_tiles_skipped": tiles_skipped,
+        "recompute_tiles_total": n_tiles,
         # tokens/s counts every token (ignored ones still cost forward work, since their LSE is
         # returned); the same over non-ignored tokens only:
         "n_valid_tokens": n_valid,
@@ -486,7 +538,8 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
         "extra_hbm_bytes": {"forward_workspace": fws_b, "backward_workspace": bws_b,
                             "tile_max": tmax_b,
-                            "per_token": (fws_b + bws_b) / N,
+                            "total": fws_b + bws_b + tmax_b,
+                            "per_token": (fws_b + bws_b + tmax_b) / N,
                             "allocator_peak_delta": int(peak_extra),
                             "logits_fp32_avoided": 4 * N * V},
         "context": {"pages_gemma2_2b": "loss memory 24 GB -> 1 MB, classifier head 28 GB -> "
