@@ -11,7 +11,7 @@ II = S.IGNORE_INDEX
 EPS = S.FILTER_EPS
 LOSS_TOL = 2e-3      # per-token loss, absolute
 GRAD_TOL = 1e-2      # dE, dC relative Frobenius
-ROW_TOL = 2e-2       # dE, dC row by row: |d row| <= ROW_TOL (|ref row| + ROW_ATOL rms row norm)
+ROW_TOL = 5e-2       # dE, dC row by row: |d row| <= ROW_TOL (|ref row| + ROW_ATOL rms row norm)
 ROW_ATOL = 1e-3
 
 
