@@ -499,11 +499,11 @@ def test_tile_maxima_match_the_logits(dtype):
     np.testing.assert_allclose(g[fin], ref[fin], rtol=1e-5, atol=1e-4)
 
 
-def _far_tiles_case(dtype, seed, V=1280, far_tiles=(1, 3)):
-    """N = 600 tokens; the given vocabulary tiles (256 rows each) get logits near -200 for
-    every token, so their G tiles can be skipped, except the one (the second far tile, token
-    tile 0) that holds token 5's target."""
-    N, D = 600, 64
+def _far_tiles_case(dtype, seed, V=1280, far_tiles=(1, 3), N=600):
+    """N tokens; the given vocabulary tiles (256 rows each) get logits near -200 for every
+    token, so their G tiles can be skipped, except the one (the second far tile, token tile 0)
+    that holds token 5's target."""
+    D = 64
     g = np.random.default_rng(seed)
     E = np.concatenate([np.full((N, 1), 10.0), 0.1 * g.standard_normal((N, D - 1))],
                        axis=1).astype(np.float32)
@@ -519,11 +519,13 @@ def _far_tiles_case(dtype, seed, V=1280, far_tiles=(1, 3)):
 
 
 FAR_LAYOUTS = {
-    # V, far vocabulary tiles: one backward chunk; or far tiles in all three chunks of
+    # V, far vocabulary tiles, N: one backward chunk; far tiles in all three chunks of
     # V = 20000 (79 tiles: chunks of tiles 0-25, 26-51, 52-78), including a chunk's first tile
-    # and the ragged last tile
-    "one_chunk": (1280, (1, 3)),
-    "three_chunks": (20000, (5, 30, 26, 60, 78)),
+    # and the ragged last tile; and 20000 tokens, two backward token blocks for bf16 inputs
+    # (three for fp32), so tiles are proved negligible from the maxima of later blocks too
+    "one_chunk": (1280, (1, 3), 600),
+    "three_chunks": (20000, (5, 30, 26, 60, 78), 600),
+    "token_blocks": (1280, (1, 3), 20000),
 }
 
 
@@ -536,21 +538,23 @@ def test_tiles_proved_negligible_skip_their_recompute(dtype, layout):
     target elsewhere qualify too), also in the G tiles computed inside the fused launches of
     later chunks, and returns bitwise the same gradients and skip counts as without them, which
     match the oracle."""
-    V0, far_tiles = FAR_LAYOUTS[layout]
-    d = _far_tiles_case(dtype, 61, V0, far_tiles)
+    V0, far_tiles, N0 = FAR_LAYOUTS[layout]
+    d = _far_tiles_case(dtype, 61, V0, far_tiles, N0)
     N, V = d["E"].shape[0], d["C"].shape[0]
-    n_vt = -(-V // 256)
+    n_vt, n_tb = -(-V // 256), -(-N // 256)
     w = S.dloss_weights(61, N)
     E, C, t = upload(d, dtype)
+    if layout == "token_blocks":
+        assert cce.backward_token_block(N, V, E.shape[1], E.dtype) < N
     tm = cce.tile_max_buffer(E, C)
     loss, lse = cce.cce_forward(E, C, t, II, tile_max=tm)
     dl = torch.from_numpy(w).to(DEV)
     # the bound, from the returned maxima: max z log2 e - min lse log2 e over valid tokens
-    tmv = tm.cpu().numpy().reshape(3, n_vt, 8).max(axis=2)
+    tmv = tm.cpu().numpy().reshape(n_tb, n_vt, 8).max(axis=2)
     l2 = lse.cpu().numpy() / math.log(2.0)
     tt = d["targets"]
     provable = provable_far = 0
-    for tb in range(3):
+    for tb in range(n_tb):
         rows = np.arange(256 * tb, min(N, 256 * tb + 256))
         ok = tt[rows] != II
         for vt in range(n_vt):
@@ -558,7 +562,7 @@ def test_tiles_proved_negligible_skip_their_recompute(dtype, layout):
             if not has_t and tmv[tb, vt] - l2[rows][ok].min() < math.log2(EPS) - 2.0 ** -10:
                 provable += 1
                 provable_far += vt in far_tiles
-    assert provable_far == 3 * len(far_tiles) - 1, provable_far
+    assert provable_far == n_tb * len(far_tiles) - 1, provable_far
     out = {}
     for name, arg in (("with", tm), ("without", None)):
         stats = torch.zeros(2, dtype=torch.int64, device=DEV)
