@@ -10,8 +10,8 @@ import torch
 import cce_synth as S
 import linear_cross_entropy_cce_amd as cce
 import oracle
-from gpu_helpers import (DEV, EPS, GRAD_TOL, II, LOSS_TOL, check_against_oracle, gpu_run, log,
-                         rel, upload)
+from gpu_helpers import (DEV, EPS, GRAD_TOL, II, LOSS_TOL, ROW_TOL, check_against_oracle,
+                         gpu_run, log, rel, row_err, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -163,6 +163,28 @@ def test_loss_mean_matches_oracle():
     assert int(nv.item()) == n
     assert abs(float(mean.item()) - m) <= LOSS_TOL
     assert rel(dE.cpu().numpy(), rE) <= GRAD_TOL and rel(dC.cpu().numpy(), rC) <= GRAD_TOL
+
+
+@pytest.mark.parametrize("gdt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_loss_mean_over_several_token_blocks(gdt):
+    """The mean call at N = 20000 (two backward token blocks, so dC adds up over the blocks in
+    the mean call's own workspace), with gradients in fp32 or bf16."""
+    d = S.small_case(20000, 64, 1280, "bf16", 93, 3.0, 1.1, 0.2)
+    E, C, t = upload(d, "bf16")
+    assert cce.backward_token_block(20000, 1280, 64, torch.bfloat16) < 20000
+    mean, nv, dE, dC = cce.cce_loss_mean(E, C, t, II, EPS, grad_dtype=gdt)
+    torch.cuda.synchronize()
+    assert dE.dtype == gdt and dC.dtype == gdt
+    m, rE, rC, n = oracle.loss_mean(d["E"], d["C"], d["targets"], II, EPS)
+    _, uE, uC, _ = oracle.loss_mean(d["E"], d["C"], d["targets"], II, 0.0)
+    gE, gC = dE.float().cpu().numpy(), dC.float().cpu().numpy()
+    log(f"[loss mean N=20000 {gdt}] mean {abs(float(mean.item()) - m):.2e} "
+        f"dE {rel(gE, rE):.2e} dC {rel(gC, rC):.2e}")
+    assert int(nv.item()) == n
+    assert abs(float(mean.item()) - m) <= LOSS_TOL
+    assert rel(gE, rE) <= GRAD_TOL and rel(gC, rC) <= GRAD_TOL
+    assert rel(gE, uE) <= GRAD_TOL and rel(gC, uC) <= GRAD_TOL
+    assert row_err(gC, rC) <= ROW_TOL
 
 
 def test_loss_mean_all_ignored_is_zero():

@@ -8,7 +8,7 @@ import torch
 import cce_synth as S
 import linear_cross_entropy_cce_amd as cce
 import oracle
-from gpu_helpers import DEV, EPS, GRAD_TOL, II, LOSS_TOL, log, rel, upload
+from gpu_helpers import DEV, EPS, GRAD_TOL, II, LOSS_TOL, ROW_TOL, log, rel, row_err, upload
 from linear_cross_entropy_cce_amd import sharded
 
 pytestmark = pytest.mark.gpu
@@ -33,6 +33,37 @@ def test_sharded_matches_oracle(bounds, eps):
     # filtered results (blocks aligned to each shard's rows) against the unfiltered oracle
     assert rel(dE.cpu().numpy(), rE) <= GRAD_TOL
     assert rel(dC.cpu().numpy(), rC) <= GRAD_TOL
+
+
+@pytest.mark.parametrize("eps", [0.0, EPS])
+def test_shards_of_several_backward_chunks(eps):
+    """Shards wider than one backward vocabulary chunk (8192 rows): each of the two shards of
+    V = 20000 runs two chunks, so chunk offsets inside a shard meet the shard's own offset in
+    the target test and in the tile maxima."""
+    N, D, V = 300, 64, 20000
+    d = S.small_case(N, D, V, "bf16", 124, 3.0, 1.1, 0.1)
+    bounds = [0, 9984, V]
+    assert all(cce.backward_chunk(N, b - a, D, torch.bfloat16) < b - a
+               for a, b in zip(bounds, bounds[1:]))
+    # targets in both chunks of both shards: each chunk's first row (chunks of 19 + 20 and
+    # 20 + 20 tiles), the rows on either side of the shard boundary, the last row
+    for i, v in enumerate((0, 4864, 8191, 9983, 9984, 15104, 19999)):
+        d["targets"][i] = v
+    E, C, t = upload(d, "bf16")
+    w = S.dloss_weights(124, N)
+    loss, lse, dE, dC = sharded.forward_backward(E, C, t, bounds, II, eps,
+                                                 dloss=torch.from_numpy(w).to(DEV))
+    torch.cuda.synchronize()
+    rl, rlse = oracle.forward(d["E"], d["C"], d["targets"], II)
+    rE, rC, _ = oracle.backward(d["E"], d["C"], d["targets"], w, II, filter_eps=0.0)
+    e_loss = np.abs(loss.cpu().numpy() - rl).max()
+    e_dE, e_dC = rel(dE.cpu().numpy(), rE), rel(dC.cpu().numpy(), rC)
+    log(f"[sharded chunks eps={eps}] loss {e_loss:.2e} dE {e_dE:.2e} dC {e_dC:.2e}")
+    assert e_loss <= LOSS_TOL
+    assert np.abs(lse.cpu().numpy() - rlse).max() <= LOSS_TOL
+    assert e_dE <= GRAD_TOL and e_dC <= GRAD_TOL
+    if eps == 0.0:
+        assert row_err(dC.cpu().numpy(), rC) <= ROW_TOL
 
 
 def test_sharded_equals_unsharded_closely():
