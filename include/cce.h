@@ -34,6 +34,14 @@
  *     N, V, D < 2^31, non-null pointers when N > 0, filter_eps and entry_floor finite and >= 0.
  *   - Limits of the gfx950 kernels (CCE_ERR_UNSUPPORTED beyond them): N <= 2^24, V <= 2^24,
  *     D <= 65536.
+ *   - Two environment variables tune the backward's plan (for measurements; unset, the plan
+ *     below applies).  Each is read once per process, when a backward is first planned, and
+ *     the workspace queries follow the same plan:
+ *       CCE_VC  vocabulary chunk rows (rounded down to a multiple of 256, at most 8192): only
+ *               narrows the chunks;
+ *       CCE_NC  token block size (rounded down to a multiple of 256, 256 .. 65536): replaces
+ *               the default 16384 (bf16) / 8192 (fp32), so the G store of the backward grows
+ *               to 2 * Nc * Vc * sizeof(dtype) bytes (up to 2 GiB for bf16) when it widens them.
  */
 #ifndef LIBCCE_CCE_H
 #define LIBCCE_CCE_H
@@ -66,7 +74,8 @@ const char* cce_status_string(cce_status s);
  *   backward: the softmax-gradient store of two (token block, vocabulary chunk) pairs in
  *             flight, 2 * Nc * Vc * sizeof(dtype) bytes with Nc <= 16384 tokens (8192 for
  *             fp32 inputs) and Vc <= 8192 columns, and their 64 x 64 block flags: bounded by a
- *             constant (at most 512 MiB), however large N and V are;
+ *             constant (at most 512 MiB unless CCE_NC widens the token blocks), however large
+ *             N and V are;
  *             + 4 * ceil(N/256) bytes (each token tile's smallest LSE);
  *             + with bf16 gradients, N * D * 4 bytes for the fp32 dE accumulator and, when N
  *               exceeds one token block, Vc * D * 4 bytes for one chunk's fp32 dC accumulator.
