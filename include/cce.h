@@ -22,8 +22,9 @@
  *     kernels move them in 16-byte vectors); a misaligned one is rejected with
  *     CCE_ERR_INVALID_ARGUMENT.  The library never allocates or frees device memory and the
  *     calls of this header keep no state between calls; scratch memory is the caller's
- *     workspace (query its size first).  (The benchmark timing hook of cce_timing.h is the
- *     one piece of process-wide state, and it is off unless started.)
+ *     workspace (query its size first).  Two exceptions: cce_forward_no_workspace keeps its
+ *     scratch in a static device array (below), and the benchmark timing hook of
+ *     cce_timing.h is process-wide state, off unless started.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work on
  *     that stream and returns; no host synchronisation happens inside.  Calls that share a
  *     workspace must not run concurrently on different streams.
