@@ -87,9 +87,11 @@ def cpu_baseline(d, w, n_tokens: int) -> dict:
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in pools] or [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in pools}))
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        cores, blas = os.cpu_count() or 1, "unknown"
     rows = np.arange(n_tokens)
     t0 = time.perf_counter()
     oracle.token_rows(d["E"], d["C"], d["targets"], rows, np.full(n_tokens, 1.0 / w.N),
@@ -97,7 +99,7 @@ def cpu_baseline(d, w, n_tokens: int) -> dict:
     dt = time.perf_counter() - t0
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {n_tokens} tokens of {w.name} (float64 forward, backward and dC "
-                      f"contribution over all V={w.V}), {dt:.1f} s"}
+                      f"contribution over all V={w.V}), {dt:.1f} s", "blas": blas}
 
 
 def vendor_gemm_reference(dev) -> dict:
