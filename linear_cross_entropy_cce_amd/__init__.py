@@ -9,7 +9,7 @@ from ._lib import (KERNEL_KINDS, LIB_PATH, CCEError, backward_chunk, backward_to
                    cce_forward_no_workspace, cce_forward_shard, cce_loss_mean, cce_merge_shards,
                    forward_no_workspace_max_bytes, forward_splits, forward_workspace_bytes, lib,
                    loss_mean_workspace_bytes, tile_max_buffer, tile_max_count, timing_begin,
-                   timing_end)
+                   timing_end, workspace)
 from .autograd import LinearCrossEntropy, linear_cross_entropy
 
 __all__ = ["LinearCrossEntropy", "linear_cross_entropy", "CCEError", "LIB_PATH", "KERNEL_KINDS",
@@ -17,4 +17,4 @@ __all__ = ["LinearCrossEntropy", "linear_cross_entropy", "CCEError", "LIB_PATH",
            "cce_backward_shard", "cce_forward", "cce_forward_no_workspace", "cce_forward_shard",
            "cce_loss_mean", "cce_merge_shards", "forward_no_workspace_max_bytes",
            "forward_splits", "forward_workspace_bytes", "lib", "loss_mean_workspace_bytes",
-           "tile_max_buffer", "tile_max_count", "timing_begin", "timing_end"]
+           "tile_max_buffer", "tile_max_count", "timing_begin", "timing_end", "workspace"]

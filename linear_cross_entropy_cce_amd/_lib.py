@@ -126,6 +126,14 @@ def _check_vec(name, t, n, dtype, dev):
         raise ValueError(f"{name} must be a contiguous {dtype} tensor [{n}] on {dev}")
 
 
+def _check_flags(dev, err_flag=None, skip_stats=None):
+    """The optional device outputs: err_flag int32 [1], skip_stats int64 [2]."""
+    if err_flag is not None:
+        _check_vec("err_flag", err_flag, 1, torch.int32, dev)
+    if skip_stats is not None:
+        _check_vec("skip_stats", skip_stats, 2, torch.int64, dev)
+
+
 def forward_workspace_bytes(N: int, V: int, D: int, dtype: torch.dtype) -> int:
     return int(lib().cce_forward_workspace_bytes(N, V, D, dtype_code(dtype)))
 
@@ -156,6 +164,15 @@ def backward_token_block(N: int, V: int, D: int, dtype: torch.dtype) -> int:
 
 def workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _workspace_arg(ws, nbytes: int, dev) -> torch.Tensor:
+    """The caller's workspace (its size is checked by the library), or a new one."""
+    if ws is None:
+        return workspace(nbytes, dev)
+    if not ws.is_cuda or ws.device != dev or not ws.is_contiguous():
+        raise ValueError(f"the workspace must be a contiguous tensor on {dev}")
+    return ws
 
 
 def tile_max_count(N: int, V: int, D: int, dtype: torch.dtype) -> int:
@@ -191,7 +208,8 @@ def cce_forward(E, C, targets, ignore_index: int = -100, *, loss=None, lse=None,
     _check_vec("lse", lse, N, torch.float32, dev)
     _check_tile_max(tile_max, N, V, D, dt, dev)
     need = lib().cce_forward_workspace_bytes(N, V, D, dt)
-    ws = workspace(need, dev) if ws is None else ws
+    ws = _workspace_arg(ws, need, dev)
+    _check_flags(dev, err_flag=err_flag)
     with torch.cuda.device(dev):
         _check("cce_forward", lib().cce_forward(
             _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, _ptr(loss), _ptr(lse),
@@ -212,6 +230,7 @@ def cce_forward_no_workspace(E, C, targets, ignore_index: int = -100, *, loss=No
     _check_vec("loss", loss, N, torch.float32, dev)
     _check_vec("lse", lse, N, torch.float32, dev)
     _check_tile_max(tile_max, N, V, D, dt, dev)
+    _check_flags(dev, err_flag=err_flag)
     with torch.cuda.device(dev):
         _check("cce_forward_no_workspace", lib().cce_forward_no_workspace(
             _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, _ptr(loss), _ptr(lse),
@@ -228,8 +247,9 @@ def _grad_outputs(N, V, D, dev, grad_dtype, dE, dC):
     dE = torch.empty((N, D), dtype=gdt, device=dev) if dE is None else dE
     dC = torch.empty((V, D), dtype=gdt, device=dev) if dC is None else dC
     for name, g, shape in (("dE", dE, (N, D)), ("dC", dC, (V, D))):
-        if g.dtype != gdt or tuple(g.shape) != shape or not g.is_contiguous() or not g.is_cuda:
-            raise ValueError(f"{name} must be a contiguous {gdt} GPU tensor of shape {shape}")
+        if (g.dtype != gdt or tuple(g.shape) != shape or not g.is_contiguous() or not g.is_cuda
+                or g.device != dev):
+            raise ValueError(f"{name} must be a contiguous {gdt} tensor of shape {shape} on {dev}")
     return dE, dC, dtype_code(gdt)
 
 
@@ -242,8 +262,8 @@ def cce_backward(dloss, E, C, targets, lse, ignore_index: int = -100, filter_eps
     non-target entries of the kept blocks are dropped."""
     N, V, D, dt = _check_inputs(E, C, targets)
     dev = E.device
-    if dloss.dtype != torch.float32 or not dloss.is_cuda:
-        raise ValueError("dloss must be a float32 GPU tensor")
+    if dloss.dtype != torch.float32 or not dloss.is_cuda or dloss.device != dev:
+        raise ValueError(f"dloss must be a float32 tensor on {dev}")
     stride = 0 if dloss.numel() == 1 and N != 1 else 1
     if stride == 1 and dloss.shape != (N,):
         raise ValueError("dloss must have N elements or one")
@@ -251,7 +271,8 @@ def cce_backward(dloss, E, C, targets, lse, ignore_index: int = -100, filter_eps
     _check_tile_max(tile_max, N, V, D, dt, dev)
     dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
     need = lib().cce_backward_workspace_bytes(N, V, D, dt, gcode)
-    ws = workspace(need, dev) if ws is None else ws
+    ws = _workspace_arg(ws, need, dev)
+    _check_flags(dev, skip_stats=skip_stats)
     with torch.cuda.device(dev):
         _check("cce_backward", lib().cce_backward(
             _ptr(dloss), stride, _ptr(E), _ptr(C), _ptr(targets), _ptr(lse), _ptr(tile_max), N,
@@ -272,7 +293,8 @@ def cce_loss_mean(E, C, targets, ignore_index: int = -100, filter_eps: float = 0
     n_valid = torch.empty(1, dtype=torch.int64, device=dev)
     dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
     need = lib().cce_loss_mean_workspace_bytes(N, V, D, dt, gcode)
-    ws = workspace(need, dev) if ws is None else ws
+    ws = _workspace_arg(ws, need, dev)
+    _check_flags(dev, err_flag=err_flag, skip_stats=skip_stats)
     with torch.cuda.device(dev):
         _check("cce_loss_mean", lib().cce_loss_mean(
             _ptr(E), _ptr(C), _ptr(targets), N, V, D, dt, ignore_index, float(filter_eps),
@@ -293,7 +315,7 @@ def cce_forward_shard(E, C_shard, targets, vocab_offset: int, ignore_index: int 
     _check_vec("target_logit", zt, N, torch.float32, dev)
     _check_tile_max(tile_max, N, V, D, dt, dev)
     need = lib().cce_forward_workspace_bytes(N, V, D, dt)
-    ws = workspace(need, dev) if ws is None else ws
+    ws = _workspace_arg(ws, need, dev)
     with torch.cuda.device(dev):
         _check("cce_forward_shard", lib().cce_forward_shard(
             _ptr(E), _ptr(C_shard), _ptr(targets), N, V, D, dt, ignore_index, int(vocab_offset),
@@ -316,6 +338,7 @@ def cce_merge_shards(lse_shards, target_logits, targets, V_total: int, ignore_in
     lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else lse
     _check_vec("loss", loss, N, torch.float32, dev)
     _check_vec("lse", lse, N, torch.float32, dev)
+    _check_flags(dev, err_flag=err_flag)
     with torch.cuda.device(dev):
         _check("cce_merge_shards", lib().cce_merge_shards(
             _ptr(lse_shards), _ptr(target_logits), S, N, _ptr(targets), ignore_index, int(V_total),
@@ -331,8 +354,8 @@ def cce_backward_shard(dloss, E, C_shard, targets, lse, vocab_offset: int,
     shard's rows of dC)."""
     N, V, D, dt = _check_inputs(E, C_shard, targets)
     dev = E.device
-    if dloss.dtype != torch.float32 or not dloss.is_cuda:
-        raise ValueError("dloss must be a float32 GPU tensor")
+    if dloss.dtype != torch.float32 or not dloss.is_cuda or dloss.device != dev:
+        raise ValueError(f"dloss must be a float32 tensor on {dev}")
     stride = 0 if dloss.numel() == 1 and N != 1 else 1
     if stride == 1 and dloss.shape != (N,):
         raise ValueError("dloss must have N elements or one")
@@ -340,7 +363,8 @@ def cce_backward_shard(dloss, E, C_shard, targets, lse, vocab_offset: int,
     _check_tile_max(tile_max, N, V, D, dt, dev)
     dE, dC, gcode = _grad_outputs(N, V, D, dev, grad_dtype, dE, dC)
     need = lib().cce_backward_workspace_bytes(N, V, D, dt, gcode)
-    ws = workspace(need, dev) if ws is None else ws
+    ws = _workspace_arg(ws, need, dev)
+    _check_flags(dev, skip_stats=skip_stats)
     with torch.cuda.device(dev):
         _check("cce_backward_shard", lib().cce_backward_shard(
             _ptr(dloss), stride, _ptr(E), _ptr(C_shard), _ptr(targets), _ptr(lse),
