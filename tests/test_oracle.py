@@ -325,6 +325,63 @@ def test_entry_floor_closed_form_equal_rows(eps):
                                rtol=1e-12, atol=1e-12)
 
 
+def block_filter_equal_rows_closed_form(E, c, t, w, V, bn=64, bv=64):
+    """The block filter with every classifier row equal to c and eps above 1/V: every softmax
+    entry is exactly 1/V < eps, so a 64 x 64 block is kept exactly when a non-ignored token of
+    its token block has its target in its vocabulary block.  Token n of block b keeps the
+    K_b vocabulary rows of its block's kept vocabulary blocks: G_nv = dloss_n (1/V - [v = t_n])
+    for v in K_b, else 0, so dE_n = dloss_n (|K_b| / V - 1) c and
+    dC_v = sum over valid n with v in K_b(n) of dloss_n E_n / V - sum over n with t_n = v of
+    dloss_n E_n.  Returns dE, dC and the number of skipped blocks."""
+    N, D = E.shape
+    valid = t != II
+    dE = np.zeros((N, D))
+    dC = np.zeros((V, D))
+    n_vb = -(-V // bv)
+    skipped = 0
+    for b0 in range(0, N, bn):
+        rows = np.arange(b0, min(N, b0 + bn))
+        kept_vb = sorted({int(t[n]) // bv for n in rows if valid[n]})
+        skipped += n_vb - len(kept_vb)
+        K = np.concatenate([np.arange(k * bv, min(V, k * bv + bv)) for k in kept_vb]) \
+            if kept_vb else np.zeros(0, dtype=np.int64)
+        for n in rows:
+            if not valid[n]:
+                continue
+            dE[n] = w[n] * (len(K) / V - 1.0) * c
+            dC[K] += w[n] * E[n] / V
+            dC[t[n]] -= w[n] * E[n]
+    return dE, dC, skipped
+
+
+def test_block_filter_closed_form_flat_softmax():
+    """The block filter drops each entry below eps, not a bounded sum of them: on a flat
+    softmax over V > 1/eps rows (every classifier row equal, so every p = 1/V exactly) it keeps
+    only the blocks that hold a target, and the filtered gradients follow the closed form of
+    block_filter_equal_rows_closed_form, far from the unfiltered dE = 0.  A threshold just
+    below 1/V keeps every block and gives the unfiltered result."""
+    rng = np.random.default_rng(33)
+    N, V, D = 150, 200, 7          # 3 token blocks (the last ragged), 4 vocabulary blocks
+    E = rng.standard_normal((N, D))
+    c = rng.standard_normal(D)
+    C = np.tile(c, (V, 1))
+    t = rng.integers(0, V, N)
+    t[:64] = rng.integers(0, 64, 64)          # token block 0 keeps vocabulary block 0 only
+    t[[5, 70, 149]] = II
+    t[128:150] = np.where(t[128:150] == II, II, 192 + (t[128:150] % 8))   # block 2: ragged vocab block
+    w = rng.uniform(0.5, 1.5, N)
+    eps = 1.5 / V
+    dE, dC, (sk, tot) = oracle.backward(E, C, t, w, II, filter_eps=eps)
+    eE, eC, esk = block_filter_equal_rows_closed_form(E, c, t, w, V)
+    assert tot == 3 * 4 and sk == esk and sk > 0
+    np.testing.assert_allclose(dE, eE, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dC, eC, rtol=1e-10, atol=1e-12)
+    assert np.abs(dE[t != II]).max() > 0.1 * np.abs(c).max()   # far from the unfiltered 0
+    dE0, _, (sk0, _) = oracle.backward(E, C, t, w, II, filter_eps=0.5 / V)
+    assert sk0 == 0
+    np.testing.assert_allclose(dE0, 0.0, atol=1e-12)
+
+
 @pytest.mark.parametrize("scale,seed", [(1.0, 41), (3.0, 42), (8.0, 43)])
 def test_entry_floor_dropped_mass_bounds(scale, seed):
     """Dropping a set S_n of non-target entries of row n changes dE_n by

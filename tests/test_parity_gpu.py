@@ -187,6 +187,37 @@ def test_loss_mean_over_several_token_blocks(gdt):
     assert row_err(gC, rC) <= ROW_TOL
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_filter_closed_form_flat_softmax(dtype):
+    """A flat softmax over V = 20000 > 1/eps rows at the benchmarks' eps = 2^-12: with every
+    classifier row equal, every p is 1/V < eps, so only the blocks holding a target are kept
+    and the filtered gradients have a closed form (the CPU pin of the same name), far from the
+    unfiltered dE = 0 -- the regime where the block filter's approximation is not small.  The
+    GPU follows the closed form and the oracle, with the oracle's skip count."""
+    from test_oracle import block_filter_equal_rows_closed_form
+    rng = np.random.default_rng(34)
+    N, V, D = 300, 20000, 64
+    E = rng.standard_normal((N, D)).astype(np.float32)
+    c = rng.standard_normal(D).astype(np.float32)
+    if dtype == "bf16":
+        E, c = S.bf16_round(E), S.bf16_round(c)
+    C = np.tile(c, (V, 1))
+    t = rng.integers(0, V, N).astype(np.int64)
+    t[[3, 100]] = II
+    d = {"E": E, "C": C, "targets": t}
+    w = S.dloss_weights(34, N)
+    g = gpu_run(d, dtype, w, EPS)
+    eE, eC, esk = block_filter_equal_rows_closed_form(E.astype(np.float64), c.astype(np.float64),
+                                                      t, w.astype(np.float64), V)
+    dE, dC, (sk, tot) = oracle.backward(E, C, t, w, II, filter_eps=EPS)
+    assert sk == esk and g["skipped"] == sk and g["total"] == tot
+    log(f"[flat softmax {dtype}] skipped {sk}/{tot}; dE vs closed form {rel(g['dE'], eE):.2e} "
+        f"dC {rel(g['dC'], eC):.2e}; oracle vs closed form dE {rel(dE, eE):.2e}")
+    assert rel(dE, eE) <= 1e-9 and rel(dC, eC) <= 1e-9
+    assert rel(g["dE"], eE) <= GRAD_TOL and rel(g["dC"], eC) <= GRAD_TOL
+    assert row_err(g["dE"], eE) <= ROW_TOL and row_err(g["dC"], eC) <= ROW_TOL
+
+
 def test_loss_mean_all_ignored_is_zero():
     d = S.small_case(64, 64, 300, "bf16", 92, 3.0, 1.1, 0.0)
     d["targets"][:] = II
