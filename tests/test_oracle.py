@@ -13,7 +13,6 @@ import pytest
 import torch
 
 import oracle
-from oracle import cce_oracle as co
 
 II = -100
 

@@ -5,7 +5,6 @@ second call runs on what the first left in the shared scratch.  Sizes whose scra
 exceed the stated maximum are refused."""
 import ctypes
 
-import numpy as np
 import pytest
 import torch
 
