@@ -1,7 +1,9 @@
 """Seeded random cases through the C ABI against the oracle: shapes (N up to 40000, so several
 backward token blocks; V up to 30000, so several vocabulary chunks), both input dtypes, filter
 thresholds 0, 2^-12 and 1e-3, logit spreads 1 to 8, Zipf or uniform targets, ignored rows, the
-forward's tile maxima on or off, fp32 or bf16 gradients, per-token or scalar dloss.
+forward's tile maxima on or off, fp32 or bf16 gradients, per-token or scalar dloss, whole
+256-row tiles of C pushed far below the other logits (tiles the maxima prove negligible), and
+the opt-in entry floor.
 
 Criteria per case: loss and LSE to 2e-3; dE and dC to 1e-2 relative Frobenius error of the
 oracle with the same threshold, plus an absolute allowance for the fp32 resolution of a target
@@ -39,12 +41,36 @@ def draw(seed):
                 eps=float(g.choice([0.0, 2.0 ** -12, 1e-3])),
                 c_scale=float(g.choice([1.0, 3.0, 8.0])), zipf=[None, 1.1][int(g.integers(0, 2))],
                 ign=float(g.choice([0.0, 0.2])), tmax=bool(g.integers(0, 2)),
-                gdt=["f32", "bf16"][int(g.integers(0, 2))], scalar=bool(g.random() < 0.2))
+                gdt=["f32", "bf16"][int(g.integers(0, 2))], scalar=bool(g.random() < 0.2),
+                far=float(g.choice([0.0, 0.0, 0.3, 0.7])),
+                floor=float(g.choice([0.0, 0.0, 0.0, 1e-6, 1e-4])))
+
+
+def far_tiles(d, c):
+    """Pushes a random fraction c["far"] of C's 256-row tiles about 32 below every other logit
+    (E[:, 0] = 8, C[v, 0] = -4 there) and moves the targets out of them."""
+    g = np.random.default_rng(c["seed"] + 7)
+    V = c["V"]
+    far = np.nonzero(g.random(-(-V // 256)) < c["far"])[0]
+    if len(far) == 0:
+        return d
+    E, C, tg = d["E"].copy(), d["C"].copy(), d["targets"].copy()
+    E[:, 0] = 8.0
+    rows = np.concatenate([np.arange(v * 256, min(V, v * 256 + 256)) for v in far])
+    C[rows, 0] = -4.0
+    if c["dtype"] == "bf16":
+        E, C = S.bf16_round(E), S.bf16_round(C)
+    near = np.setdiff1d(np.arange(V), rows)
+    bad = (tg >= 0) & np.isin(tg, rows)
+    tg[bad] = g.choice(near, size=int(bad.sum())) if len(near) else II
+    return {"E": E, "C": C, "targets": tg}
 
 
 def run_case(c):
     d = S.small_case(c["N"], c["D"], c["V"], c["dtype"], c["seed"], c["c_scale"], c["zipf"],
                      c["ign"])
+    if c["far"] > 0:
+        d = far_tiles(d, c)
     tdt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
     E = torch.from_numpy(d["E"]).to(DEV, tdt)
     C = torch.from_numpy(d["C"]).to(DEV, tdt)
@@ -61,13 +87,14 @@ def run_case(c):
     st = torch.zeros(2, dtype=torch.int64, device=DEV)
     gdt = torch.bfloat16 if c["gdt"] == "bf16" else torch.float32
     dE, dC = cce.cce_backward(dl, E, C, t, lse, II, c["eps"], tile_max=tm, grad_dtype=gdt,
-                              skip_stats=st)
+                              skip_stats=st, entry_floor=c["floor"])
     torch.cuda.synchronize()
     gl, gs = loss.cpu().numpy(), lse.cpu().numpy()
     gE, gC = dE.float().cpu().numpy(), dC.float().cpu().numpy()
     tg = d["targets"]
     rl, rs = oracle.forward(d["E"], d["C"], tg, II)
-    rE, rC, (sk, tot) = oracle.backward(d["E"], d["C"], tg, w, II, filter_eps=c["eps"])
+    rE, rC, (sk, tot) = oracle.backward(d["E"], d["C"], tg, w, II, filter_eps=c["eps"],
+                                        entry_floor=c["floor"])
     fail = []
     if np.abs(gl - rl).max() > LOSS_TOL or np.abs(gs - rs).max() > LOSS_TOL:
         fail.append("loss/lse")
