@@ -54,15 +54,25 @@
 extern "C" {
 #endif
 
+/* The two enums are int-sized, and their range sentinels make every int value a valid object
+ * of the type, so a caller's out-of-range value (which the calls reject) is never undefined in
+ * the library's C++. */
 typedef enum {
   CCE_OK = 0,
   CCE_ERR_INVALID_ARGUMENT = 1,
   CCE_ERR_UNSUPPORTED = 2,
   CCE_ERR_WORKSPACE_TOO_SMALL = 3,
-  CCE_ERR_HIP = 4
+  CCE_ERR_HIP = 4,
+  CCE_STATUS_RANGE_MIN_ = -0x7fffffff - 1,
+  CCE_STATUS_RANGE_MAX_ = 0x7fffffff
 } cce_status;
 
-typedef enum { CCE_F32 = 0, CCE_BF16 = 1 } cce_dtype;
+typedef enum {
+  CCE_F32 = 0,
+  CCE_BF16 = 1,
+  CCE_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+  CCE_DTYPE_RANGE_MAX_ = 0x7fffffff
+} cce_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* cce_status_string(cce_status s);
