@@ -361,6 +361,7 @@ const char* cce_status_string(cce_status s) {
     case CCE_ERR_UNSUPPORTED: return "CCE_ERR_UNSUPPORTED";
     case CCE_ERR_WORKSPACE_TOO_SMALL: return "CCE_ERR_WORKSPACE_TOO_SMALL";
     case CCE_ERR_HIP: return "CCE_ERR_HIP";
+    default: break;
   }
   return "CCE_ERR_UNKNOWN";
 }
