@@ -366,6 +366,7 @@ def test_block_filter_closed_form_flat_softmax():
     C = np.tile(c, (V, 1))
     t = rng.integers(0, V, N)
     t[:64] = rng.integers(0, 64, 64)          # token block 0 keeps vocabulary block 0 only
+    t[80] = 128                                # a target on a block's first row
     t[[5, 70, 149]] = II
     t[128:150] = np.where(t[128:150] == II, II, 192 + (t[128:150] % 8))   # block 2: ragged vocab block
     w = rng.uniform(0.5, 1.5, N)

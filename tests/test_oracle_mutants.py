@@ -2,8 +2,8 @@
 
 This shows the pins in test_oracle.py are sensitive to the plausible errors they are meant to
 catch: a missing max-subtraction, a sign error, a wrong index, a dropped term, an ignored
-target in the block filter, a forgotten ignore mask, an entry floor that drops targets or
-compares the wrong quantity."""
+target in the block filter, a forgotten ignore mask, a target test that also claims the next
+block, an entry floor that drops targets or compares the wrong quantity."""
 import numpy as np
 import pytest
 
@@ -88,3 +88,20 @@ def test_mutant_entry_floor_compares_the_gradient(monkeypatch):
     monkeypatch.setattr(co, "entry_negligible", bad)
     with pytest.raises(AssertionError):
         T.test_entry_floor_closed_form_equal_rows(0.0)
+
+
+def test_mutant_target_claims_the_next_block(monkeypatch):
+    """A target on the first row of a vocabulary block also keeps the block before it (an
+    inclusive upper bound in the target test)."""
+    def bad(P, t_rows, valid_rows, eps, n0, v0, bn, bv):
+        out = _orig_neg(P, t_rows, valid_rows, eps, n0, v0, bn, bv)
+        for i in range(out.shape[0]):
+            r = slice(i * bn, (i + 1) * bn)
+            tv = t_rows[r][valid_rows[r]] - v0
+            for j in range(out.shape[1]):
+                if np.any(tv == (j + 1) * bv):
+                    out[i, j] = False
+        return out
+    monkeypatch.setattr(co, "block_negligible", bad)
+    with pytest.raises(AssertionError):
+        T.test_block_filter_closed_form_flat_softmax()
