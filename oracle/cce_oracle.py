@@ -18,8 +18,7 @@ What is computed (all in float64, logits materialised one chunk at a time, never
   G[n, v]   = dloss[n] * (p[n, v] - [v == t[n]]) for valid n, 0 for ignored n
   dE        = G @ C,     dC = G^T @ E                         gradients of sum_n dloss[n] loss[n]
 
-Gradient filtering (s9: leave out the parts of the gradient computation whose contribution is
-negligible).  The pages give neither a threshold nor a granularity.  Reading used here: the
+Gradient filtering (s9: gradient terms too small to matter are dropped).  The pages give neither a threshold nor a granularity.  Reading used here: the
 token x vocab plane is cut into aligned blocks of block_n x block_v (64 x 64 by default, the
 granularity the GPU library reports); a block is negligible iff every valid token row n in it
 has p[n, v] < filter_eps for every v in it AND no valid row's target lies in it.  Negligible
@@ -34,7 +33,9 @@ and row v of dC by at most entry_floor * sum_n dloss[n] |E[n]|.
 
 Pins: every function here is checked in tests/test_oracle.py against mpmath brute force,
 closed forms, invariants, finite differences and torch's CPU cross-entropy; the block filter
-is checked against a pure-Python loop and constructed far-away blocks; the entry floor against
+is checked against a pure-Python loop, constructed far-away blocks and the closed form of a
+flat softmax (equal classifier rows, eps above 1/V: only target-holding blocks survive); the
+entry floor against
 the closed form of equal classifier rows (every p = 1/V exactly, so a floor just above or just
 below 1/V drops every non-target entry or none) and the dropped-mass bounds above.
 """
